@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the per-token NVFP4 routed-MoE hot path on one MI355X.
+
+One step = pmoe_quantize_input_per_token + pmoe_routed_moe (routing, FC1 +
+activation, requantization, FC2, fixed-order finalize) over one batch of
+synthetic tokens already resident in HBM, with weights prepared beforehand
+(preparation is timed separately and reported as `prepare`).
+
+Default workload: the one-GPU share of an EP4 MoE layer -- E=96 local experts,
+H=7168, I=3072, SwiGLU, top-6, T=1024 tokens, two hot experts (router logits
++2 on experts 0 and 48); inputs from the seeded generator in synth/.
+
+Prints one JSON line. `roofline` is the dominant kernel (FC1 grouped GEMM):
+algorithmic bytes per launch over its average duration, measured here with
+HIP events around that step on the stream it runs on. `cpu_baseline` times
+the CPU oracle on a bounded sample (all routes of two experts).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE tokens/s + effective TFLOPS (% MFMA peak), H7168/I3072 top-6, 1 GPU"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense FP16/BF16 MFMA
+NVFP4_BYTES = 9.0 / 16.0     # packed E2M1 + one E4M3 scale per 16 elements
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ep4_t1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, counts, T, R):
+    """Bytes each step must move at least (weights of active experts once, activations once)."""
+    active = int(np.count_nonzero(counts))
+    fc1_w = active * w.N1 * w.H * NVFP4_BYTES + active * 4
+    fc2_w = active * w.H * w.I * NVFP4_BYTES + active * 4
+    xq = T * w.H * NVFP4_BYTES + 4 * T
+    hq = R * w.I * NVFP4_BYTES + 4 * R
+    z = R * w.H * 2
+    return {
+        "quantize": T * w.H * 2 + xq,
+        "route": T * w.K * 4 * 3,
+        "fc1": fc1_w + xq + hq,
+        "requant": 2 * hq,
+        "fc2": fc2_w + hq + z,
+        "finalize": z + T * w.K * 8 + T * w.H * 2,
+        "step": fc1_w + fc2_w + T * w.H * 2 + 2 * xq + 2 * hq + 2 * z + T * w.K * 8 + T * w.H * 2,
+    }
+
+
+def cpu_baseline(w, ids, wts):
+    """Oracle throughput on all routes of two experts (one hot, one ordinary)."""
+    import synth
+    from oracle import moe as om
+    from oracle import quant as oq
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    experts = [0, 1]
+    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    for e in experts:
+        W.expert(e)                                   # preparation is outside the timed region
+    x = synth.activations(w)
+    t0 = time.perf_counter()
+    xq, xs, xg = oq.quantize_input_per_token(x)
+    res = om.routed_moe(xq, xs, xg, ids, wts, W, w.act, experts=experts)
+    dt = time.perf_counter() - t0
+    rows = int(res.computed_rows.sum())
+    return {"value": rows / w.K / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"all {rows} routes of experts {experts} (of T*K={w.T * w.K}) incl. per-token "
+                      f"quantization of all {w.T} tokens; tokens/s = routes/K/s; {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_moe_amd as pm
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} K={w.K} act={w.act}")
+
+    # ---------------------------------------------------------------- weights
+    w1, w2 = synth.all_weights(w, device=dev)
+    w1 = w1.view(torch.bfloat16)
+    w2 = w2.view(torch.bfloat16)
+    P = pm.prepare_weights(w1, w2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        pm.prepare_weights(w1, w2, out=P)
+    e1.record()
+    torch.cuda.synchronize()
+    prep_ms = e0.elapsed_time(e1) / reps
+    elems = w.E * (w.N1 * w.H + w.H * w.I)
+    prepare = {"ms": prep_ms, "GB/s": elems * (2 + NVFP4_BYTES) / (prep_ms * 1e-3) / 1e9,
+               "note": "reads BF16 once (algorithmic; the kernel reads it twice) and writes NVFP4"}
+    log(f"[bench] prepare_weights {prep_ms:.2f} ms")
+    del w1, w2
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- inputs
+    x = synth.activations(w, device=dev).view(torch.bfloat16)
+    ids_np, wts_np = synth.router(w)
+    ids = torch.from_numpy(ids_np).to(dev)
+    wts = torch.from_numpy(wts_np).to(dev)
+    T = w.T
+    xq = torch.empty((T, w.H // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, w.H // 16), dtype=torch.uint8, device=dev)
+    xg = torch.empty((T,), dtype=torch.float32, device=dev)
+    ws = torch.empty(pm.moe_workspace_bytes(T, w.K, w.E, w.H, w.I, P.act), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, w.H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        pm.quantize_input_per_token(x, out=(xq, xs, xg))
+        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out)
+
+    # ---------------------------------------------------------------- timed region
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # ---------------------------------------------------------------- per-step events
+    names = ["quantize", "route", "fc1", "requant", "fc2", "finalize"]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = np.zeros(len(names))
+    for _ in range(args.stage_reps):
+        evs[0].record()
+        pm.quantize_input_per_token(x, out=(xq, xs, xg))
+        evs[1].record()
+        for s in range(5):
+            pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(s, s))
+            evs[s + 2].record()
+        torch.cuda.synchronize()
+        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    stage_ms = acc / args.stage_reps
+
+    views = pm.workspace_views(ws, T, w.K, w.E, w.H, w.I, P.act)
+    counts = np.diff(views["expert_offsets"].cpu().numpy())
+    R = int(counts.sum())
+    ab = algorithmic_bytes(w, counts, T, R)
+    kernels = {n: {"us": float(stage_ms[i] * 1e3),
+                   "GB/s": float(ab[n] / (stage_ms[i] * 1e-3) / 1e9)} for i, n in enumerate(names)}
+    flops = 2.0 * R * (w.N1 * w.H + w.H * w.I)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    fc1_flops = 2.0 * R * w.N1 * w.H
+    kernels["fc1"]["TFLOP/s"] = float(fc1_flops / (stage_ms[2] * 1e-3) / 1e12)
+    kernels["fc2"]["TFLOP/s"] = float(2.0 * R * w.H * w.I / (stage_ms[4] * 1e-3) / 1e12)
+    fc1_gbs = kernels["fc1"]["GB/s"]
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.K,
+                   "act": w.act, "routed_rows": R, "parallelism": "none (1 GPU)"},
+        "tflops": tflops,
+        "mfma_frac": tflops / PEAK_F16_TFLOPS,
+        "hbm_frac_step": ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": "fc1 grouped GEMM (SwiGLU epilogue)" if w.gated else
+                     "fc1 grouped GEMM (squared-ReLU epilogue)",
+                     "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": None},
+        "kernels": kernels,
+        "prepare": prepare,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(w, ids_np, wts_np)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+/*
+ * pmoe -- per-token NVFP4 routed-MoE expert path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every compute entry point enqueues HIP kernels on the caller's stream
+ * (`stream` is a hipStream_t; NULL means the legacy default stream), returns a
+ * status code, and never allocates device memory, synchronizes, or aborts.
+ * All tensors are caller-owned device buffers (the library keeps no pointer to
+ * them after the call returns and caches nothing about them). All checks run on
+ * the host before the first launch; when a call returns an error, no kernel was
+ * launched and no output was touched (PMOE_ERR_HIP is the one exception: it
+ * reports a failed launch after validation passed).
+ *
+ * Sources of the contract (three public pages):
+ *   [Megatron-LM #8262]  per-token NVFP4 squared-ReLU and SwiGLU MoE via FlashInfer
+ *                        CuTe DSL (sections: Background, What is added, How to extend,
+ *                        What is tested).
+ *   [FlashInfer #5019]   CuTe DSL NVFP4 W4A16 MegaMoE (section: Tensor and numerical
+ *                        contract).
+ *
+ * Notation: T tokens, H hidden size, I intermediate size, E local experts,
+ * K top-k, N1 = FC1 output width (2*I gated / SwiGLU, I non-gated / squared ReLU),
+ * R = number of valid routes (at most T*K).
+ *
+ * Number formats (NVFP4): E2M1 codes packed two per byte, element 2i in the low
+ * nibble; one E4M3 (fn, max 448) block scale per 16 consecutive elements along
+ * the reduction dimension; one FP32 scale per token (activations) or per expert
+ * (weights, "alpha") [Megatron-LM #8262 . Background; FlashInfer #5019 . Tensor
+ * and numerical contract]. BF16 tensors are passed as raw 16-bit storage.
+ *
+ * Shape limits of this build: H and I multiples of 64; 1 <= K <= min(32, E);
+ * 1 <= E <= 1024; T >= 0 (T == 0 is a successful no-op); T*K < 2^31.
+ */
+#ifndef PMOE_H_
+#define PMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define PMOE_OK 0
+#define PMOE_ERR_DEVICE 1    /* current device is not gfx950 (MI355X / MI350X)          */
+#define PMOE_ERR_POINTER 2   /* null, host, or misaligned pointer                       */
+#define PMOE_ERR_SHAPE 3     /* unsupported sizes, or FC1 width neither I nor 2*I         */
+#define PMOE_ERR_ACT 4       /* activation kind disagrees with the FC1 shape             */
+#define PMOE_ERR_WORKSPACE 5 /* workspace smaller than the queried size                  */
+#define PMOE_ERR_HIP 6       /* a HIP runtime call or kernel launch failed               */
+#define PMOE_ERR_ARG 7       /* any other invalid argument (unknown enum value, ...)     */
+
+/* Activation kinds. Squared ReLU is the non-gated expert, SwiGLU the gated one;
+ * SwiGLU iff FC1 has twice FC2's input width [Megatron-LM #8262 . What is added]. */
+#define PMOE_ACT_RELU2 0
+#define PMOE_ACT_SWIGLU 1
+
+/* Element type of topk_ids: signed 32- or 64-bit [FlashInfer #5019 . Tensor and
+ * numerical contract, 'Inputs/output']. */
+#define PMOE_IDS_INT32 0
+#define PMOE_IDS_INT64 1
+
+/* Library version (major*10000 + minor*100 + patch). */
+int pmoe_version(void);
+
+/* Message of the last error returned on this host thread ("" if none). The
+ * pointer stays valid until the next pmoe call on the same thread. */
+const char* pmoe_last_error(void);
+
+/* ============================================================ prepared weights
+ *
+ * Prepared (kernel-native) layout of one FC matrix with logical shape
+ * [E, N, Kd] (N output rows, Kd the reduction length; FC1: N = N1, Kd = H;
+ * FC2: N = H, Kd = I). Rows are grouped in blocks of 32 ("col blocks" p,
+ * NB = N/32), the reduction in chunks of 64 (c, KC = Kd/64):
+ *
+ *   codes  (uint8, E*N*Kd/2 bytes): byte offset
+ *            ((((e*NB + p)*KC + c)*64 + lane)*16 + j*4 + i/2
+ *          holds element k = c*64 + 16*j + 8*(lane/32) + i (nibble i%2, low first)
+ *          of row n(p, lane%32), for j in 0..3, i in 0..7.
+ *   scales (uint8, E*N*Kd/16 bytes): byte offset
+ *            (((e*NB + p)*KC + c)*32 + col)*4 + j
+ *          holds the E4M3 scale of 16-block (c*4 + j) of row n(p, col).
+ *   alpha  (float32, E values).
+ *
+ * Row map n(p, col): non-gated FC1 and FC2: n = 32*p + col. Gated FC1 (N1 = 2I)
+ * interleaves gate and up blocks so one workgroup holds both halves of a SwiGLU
+ * output: p even -> gate row 32*(p/2) + col; p odd -> up row I + 32*(p/2) + col
+ * (gate rows are [0, I), up rows [I, 2I) of the canonical FC1 [FlashInfer #5019 .
+ * Tensor and numerical contract, 'gate-then-up']).
+ *
+ * The bytes are the canonical codes/scales of the per-expert NVFP4 recipe
+ * (packed [E, N, Kd/2], linear scales [E, N, Kd/16]) permuted by this map; no
+ * value is changed and alpha is never folded into the block scales.
+ */
+
+/* Sizes in bytes of the four prepared arrays: sizes[0] FC1 codes, sizes[1] FC1
+ * scales, sizes[2] FC2 codes, sizes[3] FC2 scales (alphas are E floats each).
+ * Host only. Returns PMOE_ERR_SHAPE for unsupported sizes. */
+int pmoe_weight_bytes(int E, int N1, int H, int I, size_t sizes[4]);
+
+/* Device workspace needed by pmoe_prepare_weights (bytes). 0 on bad shapes. */
+size_t pmoe_prepare_workspace_bytes(int E, int N1, int H, int I);
+
+/*
+ * Quantize BF16 expert stacks into the prepared NVFP4 layout
+ * [Megatron-LM #8262 . What is added, 'prepare_routed_nvfp4_weights'].
+ *   w1 : BF16 [E, N1, H], gate rows then up rows when N1 == 2*I.
+ *   w2 : BF16 [E, H, I].
+ * Per expert and FC: amax over the whole matrix (gate and up together),
+ * w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale); each 16-block gets the
+ * E4M3 scale fp32(fp32(amax_b / 6) / alpha) (round to nearest even, saturating
+ * at 448) and E2M1 codes of fp32(w / fp32(dec(scale) * alpha)) (round to nearest,
+ * ties to the even code, saturating at 6). An all-zero expert gets alpha = 0 and
+ * zero bytes.
+ * Outputs are written in place, so their addresses stay valid across refreshes
+ * (in-place refit) [Megatron-LM #8262 . What is added]. Gating is detected from
+ * the shapes: N1 == 2*I gated, N1 == I non-gated, else PMOE_ERR_SHAPE.
+ * ws: at least pmoe_prepare_workspace_bytes(...) bytes of device memory.
+ * Alignment: every pointer 16-byte aligned.
+ */
+int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, int I,
+                         void* w1_codes, void* w1_scales, float* w1_alpha,
+                         void* w2_codes, void* w2_scales, float* w2_alpha,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ============================================================ activations */
+
+/*
+ * Per-token NVFP4 quantization of BF16 activations [Megatron-LM #8262 .
+ * Background; What is added, 'quantize_routed_nvfp4_input'; How to extend,
+ * 'FC1 input' and 'per_token_scale'].
+ *   x       : BF16 [T, H] (row-major, contiguous)
+ *   xq      : uint8 [T, H/2] packed E2M1 codes (canonical layout)
+ *   x_sf    : uint8 [T, H/16] E4M3 block scales
+ *   x_scale : float32 [T] per-token scale
+ * Per token: g = fp32(amax * fp32(1/2688)) (the recipe constant 1/(448*6));
+ * per 16-block: scale = E4M3(fp32(fp32(amax_b / 6) / g)), codes =
+ * E2M1(fp32(x / fp32(dec(scale) * g))); g == 0 (all-zero token) gives zero bytes.
+ * Bit-exact IEEE binary32 with denormals. Alignment: xq and x 16 bytes,
+ * x_sf 4 bytes, x_scale 4 bytes.
+ */
+int pmoe_quantize_input_per_token(const void* x, int T, int H,
+                                  void* xq, void* x_sf, float* x_scale, void* stream);
+
+/*
+ * The same per-row NVFP4 quantizer applied to FP32 rows: the requantization of
+ * the FP32 expert intermediate before FC2 [Megatron-LM #8262 . How to extend,
+ * 'fc2_input_scale'; What is tested, 4. Train-gen parity]. routed_moe runs this
+ * quantizer on its intermediate; it is exported so it can be checked alone.
+ *   h : float32 [R, L], L a multiple of 64;  hq : uint8 [R, L/2];
+ *   h_sf : uint8 [R, L/16];  h_scale : float32 [R].
+ */
+int pmoe_quantize_rows_f32(const float* h, int R, int L,
+                           void* hq, void* h_sf, float* h_scale, void* stream);
+
+/* ============================================================ routed MoE */
+
+/* Device workspace needed by pmoe_routed_moe (bytes). 0 on bad shapes. */
+size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act);
+
+/* Fields of the routed_moe workspace, for inspection (offsets in bytes). */
+#define PMOE_WS_ROW_OF_ROUTE 0   /* int32 [T*K]   expert-sorted row of route t*K+j, -1 if invalid */
+#define PMOE_WS_ROUTE_OF_ROW 1   /* int32 [T*K]   route index of each row (first R valid)        */
+#define PMOE_WS_EXPERT_OFFSETS 2 /* int32 [E+1]   first row of each local expert; [E] = R          */
+#define PMOE_WS_COUNTERS 3       /* int32 [4]     {R, number of M-tiles, 0, 0}                     */
+#define PMOE_WS_H 4              /* float32 [T*K, I]   activation output (rows < R valid)          */
+#define PMOE_WS_HQ 5             /* uint8 [T*K, I/2]   requantized intermediate codes              */
+#define PMOE_WS_H_SF 6           /* uint8 [T*K, I/16]  its E4M3 block scales                        */
+#define PMOE_WS_H_SCALE 7        /* float32 [T*K]      its per-row scales                           */
+#define PMOE_WS_Z 8              /* BF16 [T*K, H]      per-route FC2 outputs                         */
+#define PMOE_WS_NUM_FIELDS 9
+
+/* Offsets (bytes, from the workspace base) of the fields above. Host only. */
+int pmoe_moe_workspace_layout(int T, int K, int E, int H, int I, int act,
+                              size_t offsets[PMOE_WS_NUM_FIELDS]);
+
+/*
+ * Routed-MoE expert path on per-token-quantized activations: routing, FC1
+ * grouped GEMM, activation, per-row requantization, FC2 grouped GEMM, and the
+ * deterministic finalize [Megatron-LM #8262 . What is added,
+ * 'flashinfer_routed_nvfp4_moe'; FlashInfer #5019 . Tensor and numerical
+ * contract, 'Compute order'].
+ *   xq, x_sf, x_scale : output of pmoe_quantize_input_per_token for [T, H]
+ *   topk_ids          : [T, K] int32 or int64 (ids_type); a route is valid iff
+ *                       expert_offset <= id < expert_offset + E, others
+ *                       (e.g. -1 fill) contribute nothing
+ *   topk_w            : float32 [T, K] routing weights, applied in the finalize
+ *   N1                : FC1 width the weights were prepared with (I or 2*I, else
+ *                       PMOE_ERR_SHAPE)
+ *   weights           : the six prepared arrays of pmoe_prepare_weights
+ *   act               : PMOE_ACT_RELU2 (needs N1 == I) or PMOE_ACT_SWIGLU (needs
+ *                       N1 == 2*I); a disagreement is PMOE_ERR_ACT
+ *   ws                : at least pmoe_moe_workspace_bytes(T, K, E, H, I, act) bytes
+ *   out               : BF16 [T, H]
+ * Per valid route (token t, expert e), row r:
+ *   y = fp32(sum_k dec(xq[t,k]) * dec(W1[e,:,k])) * fp32(x_scale[t] * alpha1[e])
+ *   h = max(y,0)^2  or  silu(y_gate) * y_up, in FP32
+ *   (hq, h_sf, h_scale) = per-row quantization of h (as pmoe_quantize_rows_f32)
+ *   z = bf16(fp32(sum_k dec(hq) * dec(W2[e])) * fp32(h_scale[r] * alpha2[e]))
+ * and out[t] = bf16(sum over slots j = 0..K-1 in order of fp32(w[t,j] * z)),
+ * accumulated in FP32 from +0 without fused multiply-add. A token with no
+ * valid route gets +0. The result of a token depends only on its own inputs
+ * (batch invariant): the tiling never depends on T and no split-K is used.
+ * Alignment: every pointer 16 bytes, except x_scale/topk_w/topk_ids 4 bytes.
+ */
+int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
+                    const void* topk_ids, int ids_type, const float* topk_w,
+                    int T, int K, int E, int H, int I, int N1, int expert_offset,
+                    const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                    const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                    int act, void* ws, size_t ws_bytes, void* out, void* stream);
+
+/* Steps of pmoe_routed_moe, for callers that time or interleave them. */
+#define PMOE_STEP_ROUTE 0    /* histogram, scan, tile list, scatter (3 kernels)   */
+#define PMOE_STEP_FC1 1      /* FC1 grouped GEMM + activation -> h                */
+#define PMOE_STEP_REQUANT 2  /* per-row requantization of h -> hq, h_sf, h_scale  */
+#define PMOE_STEP_FC2 3      /* FC2 grouped GEMM -> z                            */
+#define PMOE_STEP_FINALIZE 4 /* fixed-order finalize -> out                      */
+
+/*
+ * Runs steps first..last (inclusive) of pmoe_routed_moe with the same
+ * arguments and workspace; pmoe_routed_moe is steps 0..4. A step reads what the
+ * earlier steps left in the workspace, so running the steps one range after
+ * another on the same stream gives exactly the result of one full call.
+ * PMOE_ERR_ARG unless 0 <= first <= last <= 4.
+ */
+int pmoe_routed_moe_steps(int first, int last,
+                          const void* xq, const void* x_sf, const float* x_scale,
+                          const void* topk_ids, int ids_type, const float* topk_w,
+                          int T, int K, int E, int H, int I, int N1, int expert_offset,
+                          const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                          const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                          int act, void* ws, size_t ws_bytes, void* out, void* stream);
+
+/*
+ * Deterministic two-stage finalize, standalone [Megatron-LM #8262 . Background,
+ * 'two-stage finalize'; FlashInfer #5019 . Tensor and numerical contract]:
+ *   out[t, :] = bf16( sum_{j=0..K-1, row(t,j) >= 0} fp32(w[t,j] * z[row(t,j), :]) )
+ * in FP32 from +0, slot order, no fused multiply-add, one BF16 rounding.
+ *   z : BF16 [R, H];  row_of_route : int32 [T*K] (-1 = skip; values must be < R);
+ *   topk_w : float32 [T, K];  out : BF16 [T, H].
+ * H must be a multiple of 8. Alignment: z and out 16 bytes, others 4 bytes.
+ */
+int pmoe_finalize(const void* z, const int32_t* row_of_route, const float* topk_w,
+                  int T, int K, int H, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMOE_H_ */

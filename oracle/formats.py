@@ -42,15 +42,15 @@ def e2m1_encode(v):
     (between codes c and c+1) with a > m_c, or a == m_c when c+1 is even.
     """
     v = np.asarray(v, dtype=np.float32)
-    a = np.abs(v).astype(np.float64)
+    a = np.abs(v)                      # every midpoint is exact in float32
     code = np.zeros(a.shape, dtype=np.uint8)
     for c in range(7):
-        mid = 0.5 * (E2M1_MAGNITUDES[c] + E2M1_MAGNITUDES[c + 1])
+        mid = np.float32(0.5 * (E2M1_MAGNITUDES[c] + E2M1_MAGNITUDES[c + 1]))
         tie_goes_up = ((c + 1) % 2) == 0
-        passed = (a > mid) | ((a == mid) & tie_goes_up)
-        code += passed.astype(np.uint8)
-    sign = np.signbit(v).astype(np.uint8)
-    return (code | (sign << 3)).astype(np.uint8)
+        passed = (a >= mid) if tie_goes_up else (a > mid)
+        code += passed
+    code |= np.signbit(v).view(np.uint8) << np.uint8(3)
+    return code
 
 
 def pack_nibbles(codes):

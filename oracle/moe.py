@@ -205,12 +205,14 @@ class MoeResult:
 
 
 def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights, act, expert_offset=0,
-               tokens=None):
+               tokens=None, experts=None):
     """S2..S6 of the path on per-token-quantized activations.
 
     `weights` is a Weights or LazyWeights. `tokens` (optional) restricts the
     computation to a subset of tokens; every token's result depends only on
     its own row and routes, so the subset is exact and the other outputs are 0.
+    `experts` (optional) restricts the per-route rows (h, hq, z) to the given
+    local experts; the finalized output is then not computed (zeros).
     """
     E, N1, H, I = weights.shape
     gated = detect_gating(N1, I)
@@ -223,6 +225,9 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights, act, expert_offset=
     tok_of_row = rt.route_of_row // K
     want = np.ones(T, bool) if tokens is None else np.isin(np.arange(T), np.asarray(tokens))
     row_on = want[tok_of_row] if R else np.zeros(0, bool)
+    if experts is not None and R:
+        exp_of_row = np.repeat(np.arange(E), rt.counts)
+        row_on &= np.isin(exp_of_row, np.asarray(experts))
 
     h = np.zeros((R, I), F32)
     for e in range(E):
@@ -252,7 +257,7 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights, act, expert_offset=
         zf = fc(hq[rows], h_sf[rows], h_scale[rows], w2q, w2sf, a2)
         z[rows] = f32_to_bf16_rne(zf)
 
-    if R:
+    if R and experts is None:
         out = finalize(z, rt.row_of_route, topk_w, T, K)
     else:
         out = np.zeros((T, H), np.uint16)

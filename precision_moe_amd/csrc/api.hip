@@ -1,0 +1,379 @@
+// C ABI of the pmoe library: host-side validation and launch sequencing.
+// No kernel lives here. Every entry point validates all of its arguments on
+// the host before the first launch, enqueues on the caller's stream, and
+// never allocates device memory or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/pmoe.h"
+#include "kernels.h"
+
+#define PMOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace pmoe;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PMOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ------------------------------------------------------------------ device check
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PMOE_ERR_DEVICE, "no HIP device is current");
+  if (dev < 0 || dev >= 64) return fail(PMOE_ERR_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(PMOE_ERR_DEVICE, "hipGetDeviceProperties failed");
+    cached[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 2;
+    if (cached[dev] == 2) {
+      g_last_error = std::string("pmoe needs a gfx950 GPU (MI355X / MI350X); current device is ") +
+                     prop.gcnArchName;
+      return PMOE_ERR_DEVICE;
+    }
+  }
+  if (cached[dev] != 1) return fail(PMOE_ERR_DEVICE, "pmoe needs a gfx950 GPU (MI355X / MI350X)");
+  return PMOE_OK;
+}
+
+// ------------------------------------------------------------------ pointer check
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (p == nullptr) return fail(PMOE_ERR_POINTER, std::string(name) + " is null");
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(PMOE_ERR_POINTER, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return fail(PMOE_ERR_POINTER, std::string(name) + " is not a HIP device pointer");
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(PMOE_ERR_POINTER, std::string(name) + " is not device memory");
+  return PMOE_OK;
+}
+
+#define PMOE_TRY(expr)          \
+  do {                          \
+    int _rc = (expr);           \
+    if (_rc != PMOE_OK) return _rc; \
+  } while (0)
+
+#define PMOE_HIP(expr)                                                                    \
+  do {                                                                                    \
+    hipError_t _e = (expr);                                                               \
+    if (_e != hipSuccess) return fail(PMOE_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(_e)); \
+  } while (0)
+
+// ------------------------------------------------------------------ shapes
+bool dim_ok(int v) { return v > 0 && v % kChunk == 0; }
+
+int check_weight_shape(int E, int N1, int H, int I) {
+  if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a positive multiple of 64");
+  if (N1 != I && N1 != 2 * I)
+    return fail(PMOE_ERR_SHAPE, "FC1 width N1 must be I (squared ReLU) or 2*I (SwiGLU)");
+  return PMOE_OK;
+}
+
+struct WeightBytes {
+  size_t w1q, w1s, w2q, w2s;
+};
+WeightBytes weight_bytes(int E, int N1, int H, int I) {
+  WeightBytes b;
+  b.w1q = (size_t)E * N1 * H / 2;
+  b.w1s = (size_t)E * N1 * H / 16;
+  b.w2q = (size_t)E * H * I / 2;
+  b.w2s = (size_t)E * H * I / 16;
+  return b;
+}
+
+size_t prepare_ws(int E, int N1, int H, int I) {
+  return align_up((size_t)E * weight_amax_parts((long)N1 * H) * 4) +
+         align_up((size_t)E * weight_amax_parts((long)H * I) * 4);
+}
+
+// routed_moe workspace layout
+struct MoeLayout {
+  size_t off[PMOE_WS_NUM_FIELDS];
+  size_t rank_local, block_counts, tiles;
+  size_t total;
+  int max_tiles;
+};
+
+MoeLayout moe_layout(int T, int K, int E, int H, int I) {
+  MoeLayout L;
+  const size_t TK = (size_t)T * K;
+  L.max_tiles = (int)((TK + kTileM - 1) / kTileM) + E;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.off[PMOE_WS_ROW_OF_ROUTE] = take(TK * 4);
+  L.off[PMOE_WS_ROUTE_OF_ROW] = take(TK * 4);
+  L.off[PMOE_WS_EXPERT_OFFSETS] = take((size_t)(E + 1) * 4);
+  L.off[PMOE_WS_COUNTERS] = take(16);
+  L.off[PMOE_WS_H] = take(TK * I * 4);
+  L.off[PMOE_WS_HQ] = take(TK * I / 2);
+  L.off[PMOE_WS_H_SF] = take(TK * I / 16);
+  L.off[PMOE_WS_H_SCALE] = take(TK * 4);
+  L.off[PMOE_WS_Z] = take(TK * H * 2);
+  L.rank_local = take(TK * 4);
+  L.block_counts = take((size_t)route_blocks((int)TK) * E * 4);
+  L.tiles = take((size_t)L.max_tiles * 2 * 4);
+  L.total = o;
+  return L;
+}
+
+int check_moe_shape(int T, int K, int E, int H, int I, int act) {
+  if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
+  if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
+  if (K < 1 || K > 32 || K > E) return fail(PMOE_ERR_SHAPE, "K must be in [1, min(32, E)]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a positive multiple of 64");
+  if ((long long)T * K >= (1LL << 31) / 2) return fail(PMOE_ERR_SHAPE, "T*K too large");
+  if (act != PMOE_ACT_RELU2 && act != PMOE_ACT_SWIGLU) return fail(PMOE_ERR_ACT, "unknown activation kind");
+  return PMOE_OK;
+}
+
+}  // namespace
+
+// ================================================================== exports
+
+PMOE_EXPORT int pmoe_version(void) { return 100; }
+
+PMOE_EXPORT const char* pmoe_last_error(void) { return g_last_error.c_str(); }
+
+PMOE_EXPORT int pmoe_weight_bytes(int E, int N1, int H, int I, size_t sizes[4]) {
+  if (!sizes) return fail(PMOE_ERR_ARG, "sizes is null");
+  PMOE_TRY(check_weight_shape(E, N1, H, I));
+  WeightBytes b = weight_bytes(E, N1, H, I);
+  sizes[0] = b.w1q;
+  sizes[1] = b.w1s;
+  sizes[2] = b.w2q;
+  sizes[3] = b.w2s;
+  return ok();
+}
+
+PMOE_EXPORT size_t pmoe_prepare_workspace_bytes(int E, int N1, int H, int I) {
+  if (check_weight_shape(E, N1, H, I) != PMOE_OK) return 0;
+  return prepare_ws(E, N1, H, I);
+}
+
+PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, int I,
+                                     void* w1_codes, void* w1_scales, float* w1_alpha,
+                                     void* w2_codes, void* w2_scales, float* w2_alpha, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  PMOE_TRY(check_weight_shape(E, N1, H, I));
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(w1, 16, "w1"));
+  PMOE_TRY(check_ptr(w2, 16, "w2"));
+  PMOE_TRY(check_ptr(w1_codes, 16, "w1_codes"));
+  PMOE_TRY(check_ptr(w1_scales, 16, "w1_scales"));
+  PMOE_TRY(check_ptr(w1_alpha, 4, "w1_alpha"));
+  PMOE_TRY(check_ptr(w2_codes, 16, "w2_codes"));
+  PMOE_TRY(check_ptr(w2_scales, 16, "w2_scales"));
+  PMOE_TRY(check_ptr(w2_alpha, 4, "w2_alpha"));
+  PMOE_TRY(check_ptr(ws, 16, "ws"));
+  const size_t need = prepare_ws(E, N1, H, I);
+  if (ws_bytes < need)
+    return fail(PMOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part1 = static_cast<float*>(ws);
+  float* part2 = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          align_up((size_t)E * weight_amax_parts((long)N1 * H) * 4));
+  const int gated_I = (N1 == 2 * I) ? I : 0;
+  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w1), E, N1, H, gated_I, part1,
+                             static_cast<uint8_t*>(w1_codes), static_cast<uint8_t*>(w1_scales),
+                             w1_alpha, s));
+  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w2), E, H, I, 0, part2,
+                             static_cast<uint8_t*>(w2_codes), static_cast<uint8_t*>(w2_scales),
+                             w2_alpha, s));
+  return ok();
+}
+
+PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void* xq, void* x_sf,
+                                              float* x_scale, void* stream) {
+  if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(x, 16, "x"));
+  PMOE_TRY(check_ptr(xq, 16, "xq"));
+  PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
+  PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  PMOE_HIP(launch_quantize_bf16(x, T, H, static_cast<uint8_t*>(xq), static_cast<uint8_t*>(x_sf),
+                                x_scale, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, void* h_sf,
+                                       float* h_scale, void* stream) {
+  if (R < 0) return fail(PMOE_ERR_SHAPE, "R must be >= 0");
+  if (!dim_ok(L)) return fail(PMOE_ERR_SHAPE, "L must be a positive multiple of 64");
+  if (R == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(h, 16, "h"));
+  PMOE_TRY(check_ptr(hq, 16, "hq"));
+  PMOE_TRY(check_ptr(h_sf, 4, "h_sf"));
+  PMOE_TRY(check_ptr(h_scale, 4, "h_scale"));
+  PMOE_HIP(launch_quantize_f32(h, R, nullptr, L, static_cast<uint8_t*>(hq),
+                               static_cast<uint8_t*>(h_sf), h_scale, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+PMOE_EXPORT size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act) {
+  if (check_moe_shape(T, K, E, H, I, act) != PMOE_OK) return 0;
+  return moe_layout(T, K, E, H, I).total;
+}
+
+PMOE_EXPORT int pmoe_moe_workspace_layout(int T, int K, int E, int H, int I, int act,
+                                          size_t offsets[PMOE_WS_NUM_FIELDS]) {
+  if (!offsets) return fail(PMOE_ERR_ARG, "offsets is null");
+  PMOE_TRY(check_moe_shape(T, K, E, H, I, act));
+  MoeLayout L = moe_layout(T, K, E, H, I);
+  for (int i = 0; i < PMOE_WS_NUM_FIELDS; ++i) offsets[i] = L.off[i];
+  return ok();
+}
+
+PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const void* x_sf,
+                                      const float* x_scale, const void* topk_ids, int ids_type,
+                                      const float* topk_w, int T, int K, int E, int H, int I, int N1,
+                                      int expert_offset, const void* w1_codes,
+                                      const void* w1_scales, const float* w1_alpha,
+                                      const void* w2_codes, const void* w2_scales,
+                                      const float* w2_alpha, int act, void* ws, size_t ws_bytes,
+                                      void* out, void* stream) {
+  if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
+    return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
+  PMOE_TRY(check_moe_shape(T, K, E, H, I, act));
+  if (N1 != I && N1 != 2 * I) return fail(PMOE_ERR_SHAPE, "FC1 width N1 must be I or 2*I");
+  if ((N1 == 2 * I) != (act == PMOE_ACT_SWIGLU))
+    return fail(PMOE_ERR_ACT, act == PMOE_ACT_SWIGLU ? "SwiGLU needs a gated FC1 (N1 == 2*I)"
+                                                      : "squared ReLU needs a non-gated FC1 (N1 == I)");
+  if (ids_type != PMOE_IDS_INT32 && ids_type != PMOE_IDS_INT64)
+    return fail(PMOE_ERR_ARG, "ids_type must be PMOE_IDS_INT32 or PMOE_IDS_INT64");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(xq, 16, "xq"));
+  PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
+  PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  PMOE_TRY(check_ptr(topk_ids, ids_type == PMOE_IDS_INT64 ? 8 : 4, "topk_ids"));
+  PMOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  PMOE_TRY(check_ptr(w1_codes, 16, "w1_codes"));
+  PMOE_TRY(check_ptr(w1_scales, 16, "w1_scales"));
+  PMOE_TRY(check_ptr(w1_alpha, 4, "w1_alpha"));
+  PMOE_TRY(check_ptr(w2_codes, 16, "w2_codes"));
+  PMOE_TRY(check_ptr(w2_scales, 16, "w2_scales"));
+  PMOE_TRY(check_ptr(w2_alpha, 4, "w2_alpha"));
+  PMOE_TRY(check_ptr(ws, 256, "ws"));
+  PMOE_TRY(check_ptr(out, 16, "out"));
+  const MoeLayout L = moe_layout(T, K, E, H, I);
+  if (ws_bytes < L.total)
+    return fail(PMOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  const int TK = T * K;
+  char* base = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  RouteBuffers rb;
+  rb.rank_local = reinterpret_cast<int*>(base + L.rank_local);
+  rb.block_counts = reinterpret_cast<int*>(base + L.block_counts);
+  rb.expert_offsets = reinterpret_cast<int*>(base + L.off[PMOE_WS_EXPERT_OFFSETS]);
+  rb.tiles = reinterpret_cast<int*>(base + L.tiles);
+  rb.counters = reinterpret_cast<int*>(base + L.off[PMOE_WS_COUNTERS]);
+  rb.row_of_route = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROW_OF_ROUTE]);
+  rb.route_of_row = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROUTE_OF_ROW]);
+  auto run = [&](int step) { return first <= step && step <= last; };
+  if (run(PMOE_STEP_ROUTE))
+    PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+
+  float* h = reinterpret_cast<float*>(base + L.off[PMOE_WS_H]);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.off[PMOE_WS_HQ]);
+  uint8_t* h_sf = reinterpret_cast<uint8_t*>(base + L.off[PMOE_WS_H_SF]);
+  float* h_scale = reinterpret_cast<float*>(base + L.off[PMOE_WS_H_SCALE]);
+  uint16_t* z = reinterpret_cast<uint16_t*>(base + L.off[PMOE_WS_Z]);
+
+  FcParams p1;
+  p1.a_codes = static_cast<const uint8_t*>(xq);
+  p1.a_sf = static_cast<const uint8_t*>(x_sf);
+  p1.a_scale = x_scale;
+  p1.route_of_row = rb.route_of_row;
+  p1.topk = K;
+  p1.w_codes = static_cast<const uint8_t*>(w1_codes);
+  p1.w_scales = static_cast<const uint8_t*>(w1_scales);
+  p1.w_alpha = w1_alpha;
+  p1.NB = N1 / kColBlock;
+  p1.KC = H / kChunk;
+  p1.tiles = rb.tiles;
+  p1.expert_offsets = rb.expert_offsets;
+  p1.counters = rb.counters;
+  p1.max_tiles = L.max_tiles;
+  p1.out = h;
+  p1.out_stride = I;
+  if (run(PMOE_STEP_FC1)) PMOE_HIP(launch_fc(act == PMOE_ACT_SWIGLU ? kFc1Swiglu : kFc1Relu2, p1, s));
+
+  if (run(PMOE_STEP_REQUANT)) PMOE_HIP(launch_quantize_f32(h, TK, rb.counters, I, hq, h_sf, h_scale, s));
+
+  FcParams p2 = p1;
+  p2.a_codes = hq;
+  p2.a_sf = h_sf;
+  p2.a_scale = h_scale;
+  p2.route_of_row = nullptr;
+  p2.w_codes = static_cast<const uint8_t*>(w2_codes);
+  p2.w_scales = static_cast<const uint8_t*>(w2_scales);
+  p2.w_alpha = w2_alpha;
+  p2.NB = H / kColBlock;
+  p2.KC = I / kChunk;
+  p2.out = z;
+  p2.out_stride = H;
+  if (run(PMOE_STEP_FC2)) PMOE_HIP(launch_fc(kFc2, p2, s));
+
+  if (run(PMOE_STEP_FINALIZE))
+    PMOE_HIP(launch_finalize(z, rb.row_of_route, topk_w, T, K, H, static_cast<uint16_t*>(out), s));
+  return ok();
+}
+
+PMOE_EXPORT int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
+                                const void* topk_ids, int ids_type, const float* topk_w, int T,
+                                int K, int E, int H, int I, int N1, int expert_offset,
+                                const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                                const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                                int act, void* ws, size_t ws_bytes, void* out, void* stream) {
+  return pmoe_routed_moe_steps(PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, x_scale, topk_ids,
+                               ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes,
+                               w1_scales, w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes,
+                               out, stream);
+}
+
+PMOE_EXPORT int pmoe_finalize(const void* z, const int32_t* row_of_route, const float* topk_w, int T,
+                              int K, int H, void* out, void* stream) {
+  if (T < 0 || K < 1 || K > 32) return fail(PMOE_ERR_SHAPE, "need T >= 0 and 1 <= K <= 32");
+  if (H <= 0 || H % 8 != 0) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 8");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(z, 16, "z"));
+  PMOE_TRY(check_ptr(row_of_route, 4, "row_of_route"));
+  PMOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  PMOE_TRY(check_ptr(out, 16, "out"));
+  PMOE_HIP(launch_finalize(static_cast<const uint16_t*>(z), row_of_route, topk_w, T, K, H,
+                           static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+  return ok();
+}

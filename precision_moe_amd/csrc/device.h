@@ -1,0 +1,141 @@
+// Device-side building blocks shared by the pmoe kernels (gfx950 only).
+//
+// Number formats of the per-token NVFP4 recipe [Megatron-LM #8262 . Background]:
+// E2M1 codes (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign), E4M3 ("fn")
+// block scales (bias 7, largest finite 448 = 0x7E), one scale per 16 elements
+// along the reduction dimension [FlashInfer #5019 . Tensor and numerical contract].
+// Everything that decides a stored byte is plain IEEE binary32 arithmetic
+// (correctly rounded division, denormals kept, no contraction: the library is
+// compiled with -ffp-contract=off), so it reproduces the CPU definition bit for
+// bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmoe {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// fp32(1 / (448 * 6)): the recipe's global constant [Megatron-LM #8262 . What is added].
+constexpr float kRecipeConst = 0x1.861862p-12f;
+constexpr int kBlock = 16;  // elements per E4M3 block scale
+
+// ------------------------------------------------------------------ BF16
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ E4M3
+// Non-negative finite value (or +inf) -> E4M3fn byte: round to nearest even,
+// saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  if (v < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (v*512 is exact)
+    return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8; 8 is 2^-6 = byte 0x08
+  }
+  // Normal: round the 23-bit mantissa to 3 bits (ties to even); a carry moves
+  // into the exponent field, which is what rounding up to the next binade means.
+  uint32_t u = __float_as_uint(v);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (r >> 20) - (120u << 3);  // rebias 127 -> 7
+}
+
+// E4M3fn byte (sign ignored; never 0x7F here) -> exact float.
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ------------------------------------------------------------------ E2M1
+// float -> nibble: round to nearest, ties to the even code, saturate at 6;
+// bit 3 copies the IEEE sign (a negative value rounding to 0 gives 0x8).
+// The code is the number of midpoints passed: 0.25 1.25 2.5 5 (ties stay)
+// and 0.75 1.75 3.5 (ties go up).
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  float a = __builtin_fabsf(q);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// ------------------------------------------------------------------ block quantizer
+// One 16-element block given the row scale g (per-token scale or expert alpha):
+//   sf = E4M3_sat(fp32(fp32(amax_b / 6) / g)),  e = fp32(dec(sf) * g),
+//   q_i = E2M1(fp32(x_i / e)) if e > 0 else 0.
+// Returns the scale byte; codes go to lo (elements 0..7) and hi (8..15),
+// element 2i in the low nibble of byte i.
+__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g, uint32_t& lo,
+                                                  uint32_t& hi) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(x[i]));
+  uint32_t sf = 0;
+  float e = 0.0f;
+  if (g > 0.0f) {
+    float t = amax_b / 6.0f;
+    sf = e4m3_encode_sat(t / g);
+    e = e4m3_decode(sf) * g;
+  }
+  lo = 0;
+  hi = 0;
+  if (e > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(x[i] / e) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(x[8 + i] / e) << (4 * i);
+  }
+  return sf;
+}
+
+// ------------------------------------------------------------------ exact decode to FP16
+// Every E2M1 x E4M3 product has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in FP16 (normal range), and FP16 x FP16
+// products are exact in the FP32 MFMA accumulator. This is the decode-then-
+// accumulate order of the pages [FlashInfer #5019 . Tensor and numerical
+// contract, 'Compute order'], with FP16 as the exact carrier.
+//
+// The gfx950 FP4 -> FP16 convert applies only the exponent of its FP32 scale
+// operand, so it runs with scale 1.0 and the E4M3 block scale is applied by a
+// packed FP16 multiply (exact, see above).
+
+// Four E4M3 bytes (byte j = scale of block j) -> FP16, as two packed pairs.
+__device__ __forceinline__ void decode_scales4(uint32_t s, half2_t& s01, half2_t& s23) {
+  s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
+  s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
+}
+
+// One dword of 8 E2M1 codes (element i in nibble i) times the block scale
+// `sc` -> 8 FP16 values in element order.
+__device__ __forceinline__ half8_t decode8(uint32_t w, _Float16 sc) {
+  const half2_t s2 = {sc, sc};
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace pmoe

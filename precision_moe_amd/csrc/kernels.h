@@ -1,0 +1,68 @@
+// Internal launchers of the pmoe kernels (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmoe {
+
+constexpr int kTileM = 32;     // rows per M-tile of the grouped GEMMs (one MFMA row block)
+constexpr int kColBlock = 32;  // weight rows per prepared column block
+constexpr int kChunk = 64;     // reduction elements per prepared chunk
+constexpr int kRouteBlock = 256;
+constexpr int kMaxExperts = 1024;
+
+// ---------------------------------------------------------------- quantizers
+hipError_t launch_quantize_bf16(const void* x, int T, int H, uint8_t* xq, uint8_t* x_sf,
+                                float* x_scale, hipStream_t s);
+hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L, uint8_t* hq,
+                               uint8_t* h_sf, float* h_scale, hipStream_t s);
+
+// ---------------------------------------------------------------- weights
+int weight_amax_parts(long elems);
+hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_I, float* partials,
+                             uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t s);
+
+// ---------------------------------------------------------------- routing
+struct RouteBuffers {
+  int* rank_local;      // [TK]
+  int* block_counts;    // [route blocks][E]
+  int* expert_offsets;  // [E+1]
+  int* tiles;           // [max_tiles][2] = {expert, first local row}
+  int* counters;        // [4] = {R, tiles, 0, 0}
+  int* row_of_route;    // [TK]
+  int* route_of_row;    // [TK]
+};
+int route_blocks(int TK);
+hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_offset,
+                        const RouteBuffers& b, hipStream_t s);
+
+// ---------------------------------------------------------------- grouped GEMMs
+enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2 };
+
+struct FcParams {
+  const uint8_t* a_codes;    // A rows of Kd/2 bytes
+  const uint8_t* a_sf;       // A rows of Kd/16 bytes
+  const float* a_scale;      // per A row
+  const int* route_of_row;   // FC1: expert-sorted row -> route (A row = route / topk); FC2: null
+  int topk;
+  const uint8_t* w_codes;    // prepared layout
+  const uint8_t* w_scales;
+  const float* w_alpha;
+  int NB;                    // column blocks of 32 in this FC
+  int KC;                    // chunks of 64 along the reduction
+  const int* tiles;
+  const int* expert_offsets;
+  const int* counters;
+  int max_tiles;
+  void* out;                 // FC1: float h [rows][out_stride]; FC2: BF16 z [rows][out_stride]
+  int out_stride;
+};
+__host__ __device__ int fc_col_tiles(int NB);
+hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- finalize
+hipError_t launch_finalize(const uint16_t* z, const int* row_of_route, const float* w, int T,
+                           int K, int H, uint16_t* out, hipStream_t s);
+
+}  // namespace pmoe

@@ -1,0 +1,164 @@
+// Routing: histogram + prefix-sum permutation of the valid routes into
+// expert-contiguous rows, feeding the grouped GEMMs (the expert-sorted layout
+// the pages' block-scaled grouped GEMMs consume [Megatron-LM #8262 .
+// Background]). Deterministic by construction: integer counts only, and the
+// order is fixed -- rows of an expert follow ascending route index f = t*K + j
+// (a stable sort).
+//
+//   route_count   : per 256-route block, each valid route's rank among the
+//                   block's earlier routes to the same expert (wave ballots on
+//                   the expert id bits + per-wave counts in LDS), and the block's
+//                   per-expert counts.
+//   route_scan    : one workgroup: per expert, exclusive prefix over blocks
+//                   (in place), totals, exclusive scan over experts, and the
+//                   M-tile list {expert, first local row} (tiles of 32 rows).
+//   route_scatter : row = expert start + block prefix + in-block rank;
+//                   writes row_of_route and route_of_row.
+// A route is valid iff expert_offset <= id < expert_offset + E; other ids
+// (the -1 fill of unused slots, other ranks' experts) are skipped.
+#include "device.h"
+#include "kernels.h"
+
+namespace pmoe {
+
+int route_blocks(int TK) { return (TK + kRouteBlock - 1) / kRouteBlock; }
+
+template <typename IdT>
+__device__ __forceinline__ int local_expert(const IdT* ids, int f, int E, int offset) {
+  const long long loc = (long long)ids[f] - (long long)offset;
+  return (loc >= 0 && loc < E) ? (int)loc : -1;
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(256) void route_count_kernel(const IdT* __restrict__ ids, int TK, int E,
+                                                          int offset, int nbits,
+                                                          int* __restrict__ rank_local,
+                                                          int* __restrict__ block_counts) {
+  __shared__ int wcnt[4][kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * E; i += 256) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int f = blockIdx.x * kRouteBlock + tid;
+  const int e = f < TK ? local_expert(ids, f, E, offset) : -1;
+  // Lanes of this wave routed to the same expert: AND of per-bit ballots.
+  uint64_t match = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t set = __ballot(bit);
+    match &= bit ? set : ~set;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank_w = __popcll(match & below);
+  if (e >= 0 && rank_w == 0) wcnt[wave][e] = __popcll(match);
+  __syncthreads();
+  if (f < TK) {
+    int r = -1;
+    if (e >= 0) {
+      r = rank_w;
+      for (int w = 0; w < wave; ++w) r += wcnt[w][e];
+    }
+    rank_local[f] = r;
+  }
+  for (int x = tid; x < E; x += 256)
+    block_counts[(long)blockIdx.x * E + x] = wcnt[0][x] + wcnt[1][x] + wcnt[2][x] + wcnt[3][x];
+}
+
+// Inclusive block scan over 1024 threads (Hillis-Steele in LDS).
+__device__ __forceinline__ int block_inclusive_scan_1024(int v, int* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  return sh[tid];
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ block_counts, int NB,
+                                                          int E, int* __restrict__ expert_offsets,
+                                                          int* __restrict__ tiles,
+                                                          int* __restrict__ counters) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < NB; ++b) {
+      const int c = block_counts[(long)b * E + e];
+      block_counts[(long)b * E + e] = total;  // exclusive prefix over blocks
+      total += c;
+    }
+  }
+  const int incl = block_inclusive_scan_1024(total, sh);
+  const int start = incl - total;
+  const int R = sh[1023];
+  __syncthreads();
+  const int ntiles = (total + kTileM - 1) / kTileM;
+  const int tincl = block_inclusive_scan_1024(ntiles, sh);
+  const int tstart = tincl - ntiles;
+  if (e < E) {
+    expert_offsets[e] = start;
+    for (int i = 0; i < ntiles; ++i) {
+      tiles[2 * (tstart + i)] = e;
+      tiles[2 * (tstart + i) + 1] = i * kTileM;
+    }
+  }
+  if (e == 0) {
+    expert_offsets[E] = R;
+    counters[0] = R;
+    counters[1] = sh[1023];
+    counters[2] = 0;
+    counters[3] = 0;
+  }
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(256) void route_scatter_kernel(
+    const IdT* __restrict__ ids, int TK, int E, int offset, const int* __restrict__ rank_local,
+    const int* __restrict__ block_prefix, const int* __restrict__ expert_offsets,
+    int* __restrict__ row_of_route, int* __restrict__ route_of_row) {
+  const int f = blockIdx.x * kRouteBlock + threadIdx.x;
+  if (f >= TK) return;
+  const int r = rank_local[f];
+  if (r < 0) {
+    row_of_route[f] = -1;
+    return;
+  }
+  const int e = local_expert(ids, f, E, offset);
+  const int row = expert_offsets[e] + block_prefix[(long)blockIdx.x * E + e] + r;
+  row_of_route[f] = row;
+  route_of_row[row] = f;
+}
+
+hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_offset,
+                        const RouteBuffers& b, hipStream_t s) {
+  const int NB = route_blocks(TK);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (ids64)
+    route_count_kernel<long long><<<NB, 256, 0, s>>>(static_cast<const long long*>(ids), TK, E,
+                                                     expert_offset, nbits, b.rank_local,
+                                                     b.block_counts);
+  else
+    route_count_kernel<int><<<NB, 256, 0, s>>>(static_cast<const int*>(ids), TK, E, expert_offset,
+                                               nbits, b.rank_local, b.block_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  route_scan_kernel<<<1, 1024, 0, s>>>(b.block_counts, NB, E, b.expert_offsets, b.tiles,
+                                       b.counters);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ids64)
+    route_scatter_kernel<long long><<<NB, 256, 0, s>>>(
+        static_cast<const long long*>(ids), TK, E, expert_offset, b.rank_local, b.block_counts,
+        b.expert_offsets, b.row_of_route, b.route_of_row);
+  else
+    route_scatter_kernel<int><<<NB, 256, 0, s>>>(static_cast<const int*>(ids), TK, E, expert_offset,
+                                                 b.rank_local, b.block_counts, b.expert_offsets,
+                                                 b.row_of_route, b.route_of_row);
+  return hipGetLastError();
+}
+
+}  // namespace pmoe

@@ -1,0 +1,107 @@
+// Weight preparation: BF16 expert stacks -> NVFP4 in the prepared layout
+// [Megatron-LM #8262 . What is added, 'prepare_routed_nvfp4_weights'].
+//
+// Two kernels per FC matrix:
+//   1. amax partials: each workgroup reduces max|w| over a 64K-element span of
+//      one expert (exact and order-free, so the result is deterministic);
+//   2. quantize: each workgroup owns one 32-row column block of one expert,
+//      folds its expert's partials into amax, derives
+//        w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale)
+//      and quantizes every 16-block of its rows with g = alpha, writing codes
+//      and E4M3 scales straight into the prepared layout (see include/pmoe.h).
+// Writing into caller buffers in place keeps their addresses fixed across a
+// refresh (in-place refit).
+#include "device.h"
+#include "kernels.h"
+
+namespace pmoe {
+
+constexpr int kAmaxSpan = 256 * 256;  // elements reduced per workgroup in pass 1
+
+int weight_amax_parts(long elems) { return (int)((elems + kAmaxSpan - 1) / kAmaxSpan); }
+
+__global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __restrict__ w,
+                                                          long per_expert, int parts,
+                                                          float* __restrict__ partials) {
+  const int e = blockIdx.y, part = blockIdx.x;
+  const long begin = (long)part * kAmaxSpan;
+  const long end = begin + kAmaxSpan < per_expert ? begin + kAmaxSpan : per_expert;
+  const uint16_t* base = w + (long)e * per_expert;
+  float m = 0.0f;
+  for (long i = begin + threadIdx.x * 8; i < end; i += 256 * 8) {
+    uint4 u = *reinterpret_cast<const uint4*>(base + i);  // per_expert is a multiple of 8
+    uint32_t v[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(v[k] & 0xFFFFu)));
+      m = __builtin_fmaxf(m, __builtin_fabsf(bf16_to_f32(v[k] >> 16)));
+    }
+  }
+  __shared__ float red[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partials[(long)e * parts + part] =
+        __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
+
+// grid (NB, E). gated_I > 0 selects the gate/up interleave of a gated FC1.
+__global__ __launch_bounds__(256) void weight_quant_kernel(
+    const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int KC,
+    const float* __restrict__ partials, int parts, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ alpha_out) {
+  const int p = blockIdx.x, e = blockIdx.y;
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += 256) m = __builtin_fmaxf(m, partials[(long)e * parts + i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float w_scale = 2688.0f / amax;  // +inf for an all-zero expert
+  const float alpha = 1.0f / w_scale;    // then 0
+  if (p == 0 && threadIdx.x == 0) alpha_out[e] = alpha;
+
+  const int nkb = Kd / kBlock;
+  const long chunk_base = ((long)e * NB + p) * KC;
+  for (int idx = threadIdx.x; idx < kColBlock * nkb; idx += 256) {
+    const int col = idx / nkb, kb = idx - col * nkb;
+    int n;
+    if (gated_I > 0)
+      n = ((p & 1) ? gated_I : 0) + kColBlock * (p >> 1) + col;
+    else
+      n = kColBlock * p + col;
+    const uint4* src = reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + kb * kBlock);
+    uint4 u0 = src[0], u1 = src[1];
+    uint32_t v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+    }
+    uint32_t lo, hi;
+    const uint32_t sf = quant_block16(x, alpha, lo, hi);
+    const int c = kb >> 2, j = kb & 3;
+    uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + ((chunk_base + c) * 64) * 16);
+    cdst[col * 4 + j] = lo;         // lane col (elements 0..7 of the block)
+    cdst[(col + 32) * 4 + j] = hi;  // lane col + 32 (elements 8..15)
+    scales[((chunk_base + c) * 32 + col) * 4 + j] = (uint8_t)sf;
+  }
+}
+
+hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_I, float* partials,
+                             uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t s) {
+  const long per_expert = (long)N * Kd;
+  const int parts = weight_amax_parts(per_expert);
+  weight_amax_kernel<<<dim3(parts, E), 256, 0, s>>>(w, per_expert, parts, partials);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int NB = N / kColBlock, KC = Kd / kChunk;
+  weight_quant_kernel<<<dim3(NB, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, KC, partials, parts, codes,
+                                                  scales, alpha);
+  return hipGetLastError();
+}
+
+}  // namespace pmoe

@@ -172,10 +172,12 @@ def _bf16_np(x):
 
 
 def _bf16_t(x):
+    """float32 tensor -> BF16 bit patterns as int16 (view as torch.bfloat16 for use)."""
     import torch
     u = x.contiguous().view(torch.int32).to(torch.int64) & 0xFFFFFFFF
     r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.to(torch.int32).to(torch.uint16) if hasattr(torch, "uint16") else r.to(torch.int16)
+    r = r - ((r >> 15) << 16)                       # two's-complement int16 value of the bits
+    return r.to(torch.int16)
 
 
 def _normal_np(k1, k2, n, scale=None, bf16=False):
@@ -222,7 +224,8 @@ def _as_bf16(x, device):
 
 # ----------------------------------------------------------------------------- tensors
 def activations(w: Workload, T: int = None, device=None):
-    """BF16 activations [T, H] (uint16 bit patterns; numpy, or a torch tensor on `device`)."""
+    """BF16 activations [T, H]: numpy uint16 bit patterns, or (device given) a torch int16
+    tensor of the same bits."""
     T = w.T if T is None else T
     n = T * w.H
     x = _normal(w, T_X, 0, n, device)
@@ -267,7 +270,8 @@ def router(w: Workload, T: int = None):
 
 
 def expert_weights(w: Workload, e: int, device=None):
-    """(FC1 [N1, H], FC2 [H, I]) BF16 of local expert e; FC1 rows are gate then up."""
+    """(FC1 [N1, H], FC2 [H, I]) BF16 of local expert e; FC1 rows are gate then up.
+    numpy uint16 bit patterns, or (device given) torch int16 tensors of the same bits."""
     if device is None:
         std = np.float32(w.weight_std)
         a = _normal_np(*_keys(w, T_W1, e), w.N1 * w.H, std, bf16=True)
@@ -285,9 +289,8 @@ def all_weights(w: Workload, device=None):
         w2 = np.empty((w.E, w.H, w.I), np.uint16)
     else:
         import torch
-        dt = torch.uint16 if hasattr(torch, "uint16") else torch.int16
-        w1 = torch.empty((w.E, w.N1, w.H), dtype=dt, device=device)
-        w2 = torch.empty((w.E, w.H, w.I), dtype=dt, device=device)
+        w1 = torch.empty((w.E, w.N1, w.H), dtype=torch.int16, device=device)
+        w2 = torch.empty((w.E, w.H, w.I), dtype=torch.int16, device=device)
     for e in range(w.E):
         a, b = expert_weights(w, e, device)
         w1[e], w2[e] = a, b

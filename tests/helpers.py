@@ -1,0 +1,60 @@
+"""Test-side helpers: the prepared-weight layout map and tensor transfers.
+
+The prepared layout is documented in include/pmoe.h; `canonical_from_prepared`
+inverts it so prepared bytes can be compared with the oracle's canonical
+[E, N, K/2] codes and [E, N, K/16] scales.
+"""
+import numpy as np
+
+
+def prepared_row_map(N, gated_I):
+    """Canonical row index of each prepared row p*32 + col."""
+    NB = N // 32
+    p = np.repeat(np.arange(NB), 32)
+    col = np.tile(np.arange(32), NB)
+    if gated_I:
+        return np.where(p % 2 == 1, gated_I, 0) + 32 * (p // 2) + col
+    return 32 * p + col
+
+
+def canonical_from_prepared(codes, scales, E, N, Kd, gated_I=0):
+    NB, KC = N // 32, Kd // 64
+    c = np.asarray(codes, np.uint8).reshape(E, NB, KC, 2, 32, 4, 4)      # e p c h col j b
+    c = c.transpose(0, 1, 4, 2, 5, 3, 6).reshape(E, NB * 32, KC * 32)     # e (p col) (c j h b)
+    s = np.asarray(scales, np.uint8).reshape(E, NB, KC, 32, 4)            # e p c col j
+    s = s.transpose(0, 1, 3, 2, 4).reshape(E, NB * 32, KC * 4)
+    rows = prepared_row_map(N, gated_I)
+    cq = np.empty_like(c)
+    cs = np.empty_like(s)
+    cq[:, rows] = c
+    cs[:, rows] = s
+    return cq, cs
+
+
+def np_u8(t):
+    return t.detach().cpu().numpy().view(np.uint8) if t.dtype != __import__("torch").uint8 else t.detach().cpu().numpy()
+
+
+def bf16_bits(t):
+    """torch 2-byte tensor -> numpy uint16 bit patterns."""
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def dev_bf16(a, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def dev(a, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def per_token_close(got, want, rel):
+    """max_n |got - want| <= rel * max_n |want| for every row (want = 0 rows need got == 0)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want).max(axis=1)
+    scale = np.abs(want).max(axis=1)
+    return err <= rel * scale + (scale == 0) * 0.0, err / np.maximum(scale, 1e-30)

@@ -1,0 +1,38 @@
+"""The test-side inverse of the prepared-weight layout equals a literal,
+element-by-element construction from the layout's definition in include/pmoe.h."""
+import numpy as np
+import pytest
+
+from helpers import canonical_from_prepared, prepared_row_map
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_inverse_layout_map(gated):
+    rng = np.random.default_rng(0)
+    E, I, H = 2, 64, 128
+    gI = I if gated else 0
+    N = 2 * I if gated else I
+    canon = rng.integers(0, 256, (E, N, H // 2), dtype=np.uint8)
+    canon_s = rng.integers(0, 127, (E, N, H // 16), dtype=np.uint8)
+    NB, KC = N // 32, H // 64
+    prep = np.zeros(E * N * H // 2, np.uint8)
+    prep_s = np.zeros(E * N * H // 16, np.uint8)
+    rows = prepared_row_map(N, gI)
+    for e in range(E):
+        for p in range(NB):
+            for col in range(32):
+                n = rows[p * 32 + col]
+                if gated:
+                    assert n == (I if p % 2 else 0) + 32 * (p // 2) + col
+                for c in range(KC):
+                    for h in range(2):
+                        for j in range(4):
+                            for i in range(8):
+                                k = c * 64 + 16 * j + 8 * h + i
+                                nib = (canon[e, n, k // 2] >> (4 * (k % 2))) & 15
+                                off = (((e * NB + p) * KC + c) * 64 + col + 32 * h) * 16 + j * 4 + i // 2
+                                prep[off] |= nib << (4 * (i % 2))
+                    for j in range(4):
+                        prep_s[(((e * NB + p) * KC + c) * 32 + col) * 4 + j] = canon_s[e, n, c * 4 + j]
+    cq, cs = canonical_from_prepared(prep, prep_s, E, N, H, gI)
+    assert np.array_equal(cq, canon) and np.array_equal(cs, canon_s)

@@ -11,10 +11,10 @@ def test_numpy_and_torch_backends_agree(name):
     w = synth.WORKLOADS[name].with_(H=256, I=128)
     x = synth.activations(w, T=8)
     xt = synth.activations(w, T=8, device="cpu")
-    assert np.array_equal(x, xt.numpy())
+    assert np.array_equal(x, xt.numpy().view(np.uint16))
     a, b = synth.expert_weights(w, 2)
     at, bt = synth.expert_weights(w, 2, device="cpu")
-    assert np.array_equal(a, at.numpy()) and np.array_equal(b, bt.numpy())
+    assert np.array_equal(a, at.numpy().view(np.uint16)) and np.array_equal(b, bt.numpy().view(np.uint16))
 
 
 def test_deterministic_and_distinct_streams():
