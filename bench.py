@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="ep4_t1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes 5 times "
+                         "(calibrates the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -103,6 +106,15 @@ def main():
     import torch
     import precision_moe_amd as pm
     import synth
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_bytes} bytes 5 times")
+        return
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

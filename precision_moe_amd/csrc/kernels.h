@@ -6,7 +6,7 @@
 
 namespace pmoe {
 
-constexpr int kTileM = 32;     // rows per M-tile of the grouped GEMMs (one MFMA row block)
+constexpr int kTileM = 64;     // rows per M-tile of the grouped GEMMs (two MFMA row blocks)
 constexpr int kColBlock = 32;  // weight rows per prepared column block
 constexpr int kChunk = 64;     // reduction elements per prepared chunk
 constexpr int kRouteBlock = 256;
