@@ -27,8 +27,9 @@
  * (weights, "alpha") [Megatron-LM #8262 . Background; FlashInfer #5019 . Tensor
  * and numerical contract]. BF16 tensors are passed as raw 16-bit storage.
  *
- * Shape limits of this build: H and I multiples of 64; 1 <= K <= min(32, E);
- * 1 <= E <= 1024; T >= 0 (T == 0 is a successful no-op); T*K < 2^31.
+ * Shape limits of this build: H and I multiples of 64 in [64, 16384];
+ * 1 <= K <= min(32, E); 1 <= E <= 1024; T >= 0 (T == 0 is a successful no-op);
+ * T*H and T*K*I below 2^31.
  */
 #ifndef PMOE_H_
 #define PMOE_H_
@@ -72,14 +73,18 @@ const char* pmoe_last_error(void);
  * Prepared (kernel-native) layout of one FC matrix with logical shape
  * [E, N, Kd] (N output rows, Kd the reduction length; FC1: N = N1, Kd = H;
  * FC2: N = H, Kd = I). Rows are grouped in blocks of 32 ("col blocks" p,
- * NB = N/32), the reduction in chunks of 64 (c, KC = Kd/64):
+ * NB = N/32, padded with all-zero blocks to NBp = NB rounded up to a multiple
+ * of 8), blocks in column tiles of 8 (ct = p/8, pos = p%8, NT = NBp/8), and
+ * the reduction in chunks of 64 (c, KC = Kd/64). Chunk c of a column tile --
+ * all 8 of its blocks -- is one contiguous slab, so a GEMM workgroup owning
+ * the tile streams a single sequential region:
  *
- *   codes  (uint8, E*N*Kd/2 bytes): byte offset
- *            ((((e*NB + p)*KC + c)*64 + lane)*16 + j*4 + i/2
+ *   codes  (uint8, E*NBp*32*Kd/2 bytes): byte offset
+ *            (((((e*NT + ct)*KC + c)*8 + pos)*64 + lane)*16 + j*4 + i/2
  *          holds element k = c*64 + 16*j + 8*(lane/32) + i (nibble i%2, low first)
  *          of row n(p, lane%32), for j in 0..3, i in 0..7.
- *   scales (uint8, E*N*Kd/16 bytes): byte offset
- *            (((e*NB + p)*KC + c)*32 + col)*4 + j
+ *   scales (uint8, E*NBp*32*Kd/16 bytes): byte offset
+ *            ((((e*NT + ct)*KC + c)*8 + pos)*32 + col)*4 + j
  *          holds the E4M3 scale of 16-block (c*4 + j) of row n(p, col).
  *   alpha  (float32, E values).
  *
@@ -90,8 +95,9 @@ const char* pmoe_last_error(void);
  * Tensor and numerical contract, 'gate-then-up']).
  *
  * The bytes are the canonical codes/scales of the per-expert NVFP4 recipe
- * (packed [E, N, Kd/2], linear scales [E, N, Kd/16]) permuted by this map; no
- * value is changed and alpha is never folded into the block scales.
+ * (packed [E, N, Kd/2], linear scales [E, N, Kd/16]) permuted by this map
+ * (padding blocks are zero); no value is changed and alpha is never folded
+ * into the block scales.
  */
 
 /* Sizes in bytes of the four prepared arrays: sizes[0] FC1 codes, sizes[1] FC1
@@ -148,7 +154,7 @@ int pmoe_quantize_input_per_token(const void* x, int T, int H,
  * the FP32 expert intermediate before FC2 [Megatron-LM #8262 . How to extend,
  * 'fc2_input_scale'; What is tested, 4. Train-gen parity]. routed_moe runs this
  * quantizer on its intermediate; it is exported so it can be checked alone.
- *   h : float32 [R, L], L a multiple of 64;  hq : uint8 [R, L/2];
+ *   h : float32 [R, L], L a multiple of 64 up to 16384;  hq : uint8 [R, L/2];
  *   h_sf : uint8 [R, L/16];  h_scale : float32 [R].
  */
 int pmoe_quantize_rows_f32(const float* h, int R, int L,

@@ -11,7 +11,8 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libpmoe.so")
+# PMOE_LIB may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PMOE_LIB") or os.path.join(_HERE, "_lib", "libpmoe.so")
 
 ACT_RELU2, ACT_SWIGLU = 0, 1
 IDS_INT32, IDS_INT64 = 0, 1

@@ -81,12 +81,12 @@ int check_ptr(const void* p, size_t align, const char* name) {
   } while (0)
 
 // ------------------------------------------------------------------ shapes
-bool dim_ok(int v) { return v > 0 && v % kChunk == 0; }
+bool dim_ok(int v) { return v > 0 && v % kChunk == 0 && v <= kMaxRow; }
 
 int check_weight_shape(int E, int N1, int H, int I) {
   if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
-  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a positive multiple of 64");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a multiple of 64 in [64, 16384]");
   if (N1 != I && N1 != 2 * I)
     return fail(PMOE_ERR_SHAPE, "FC1 width N1 must be I (squared ReLU) or 2*I (SwiGLU)");
   return PMOE_OK;
@@ -97,10 +97,13 @@ struct WeightBytes {
 };
 WeightBytes weight_bytes(int E, int N1, int H, int I) {
   WeightBytes b;
-  b.w1q = (size_t)E * N1 * H / 2;
-  b.w1s = (size_t)E * N1 * H / 16;
-  b.w2q = (size_t)E * H * I / 2;
-  b.w2s = (size_t)E * H * I / 16;
+  // row counts padded to whole column tiles (8 blocks of 32 rows)
+  const size_t n1p = (size_t)padded_col_blocks(N1 / kColBlock) * kColBlock;
+  const size_t hp = (size_t)padded_col_blocks(H / kColBlock) * kColBlock;
+  b.w1q = (size_t)E * n1p * H / 2;
+  b.w1s = (size_t)E * n1p * H / 16;
+  b.w2q = (size_t)E * hp * I / 2;
+  b.w2s = (size_t)E * hp * I / 16;
   return b;
 }
 
@@ -138,7 +141,7 @@ MoeLayout moe_layout(int T, int K, int E, int H, int I) {
   L.off[PMOE_WS_Z] = take(TK * H * 2);
   L.rank_local = take(TK * 4);
   L.block_counts = take((size_t)route_blocks((int)TK) * E * 4);
-  L.tiles = take((size_t)L.max_tiles * 2 * 4);
+  L.tiles = take((size_t)L.max_tiles * 4 * 4);
   L.total = o;
   return L;
 }
@@ -147,9 +150,11 @@ int check_moe_shape(int T, int K, int E, int H, int I, int act) {
   if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
   if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
   if (K < 1 || K > 32 || K > E) return fail(PMOE_ERR_SHAPE, "K must be in [1, min(32, E)]");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
-  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a positive multiple of 64");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a multiple of 64 in [64, 16384]");
   if ((long long)T * K >= (1LL << 31) / 2) return fail(PMOE_ERR_SHAPE, "T*K too large");
+  if ((long long)T * H >= (1LL << 31) || (long long)T * K * I >= (1LL << 31))
+    return fail(PMOE_ERR_SHAPE, "T*H and T*K*I must stay below 2^31 elements");
   if (act != PMOE_ACT_RELU2 && act != PMOE_ACT_SWIGLU) return fail(PMOE_ERR_ACT, "unknown activation kind");
   return PMOE_OK;
 }
@@ -213,7 +218,7 @@ PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int 
 PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void* xq, void* x_sf,
                                               float* x_scale, void* stream) {
   if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a positive multiple of 64");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
   if (T == 0) return ok();
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(x, 16, "x"));
@@ -228,7 +233,7 @@ PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void*
 PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, void* h_sf,
                                        float* h_scale, void* stream) {
   if (R < 0) return fail(PMOE_ERR_SHAPE, "R must be >= 0");
-  if (!dim_ok(L)) return fail(PMOE_ERR_SHAPE, "L must be a positive multiple of 64");
+  if (!dim_ok(L)) return fail(PMOE_ERR_SHAPE, "L must be a multiple of 64 in [64, 16384]");
   if (R == 0) return ok();
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(h, 16, "h"));
@@ -314,6 +319,7 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
   FcParams p1;
   p1.a_codes = static_cast<const uint8_t*>(xq);
   p1.a_sf = static_cast<const uint8_t*>(x_sf);
+  p1.a_rows = T;
   p1.a_scale = x_scale;
   p1.route_of_row = rb.route_of_row;
   p1.topk = K;
@@ -335,6 +341,7 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
   FcParams p2 = p1;
   p2.a_codes = hq;
   p2.a_sf = h_sf;
+  p2.a_rows = TK;
   p2.a_scale = h_scale;
   p2.route_of_row = nullptr;
   p2.w_codes = static_cast<const uint8_t*>(w2_codes);

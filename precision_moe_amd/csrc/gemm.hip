@@ -10,15 +10,22 @@
 // with at most 32 rows skips the upper row block entirely.
 //
 // Reduction loop, in stages of 128 elements (two 64-element chunks):
-//   * A (activations: NVFP4 rows gathered by route for FC1, contiguous for
-//     FC2): each thread loads 16 bytes of codes + 2 scale bytes of one row,
-//     decodes 32 values exactly to FP16 and writes them into a double-
-//     buffered LDS stage [64 rows][128 k] (row stride 272 B).
-//   * B (weights, prepared layout): per chunk and column block each lane loads
-//     one 16-byte span (a contiguous 1 KB per wave-load) and one dword of four
-//     E4M3 scales. Loads run four chunks ahead in registers; decoding happens
-//     in registers straight into MFMA operand order, and every decoded B
-//     fragment feeds both row blocks.
+//   * A (activations, NVFP4 rows gathered by route for FC1, contiguous rows
+//     for FC2): each thread buffer-loads 16 bytes of codes (32 elements) and
+//     their two block scales of one row, decodes them exactly to FP16 and writes
+//     them into a multi-buffered LDS stage [64 rows][128 k]. Within a row the
+//     16-byte slots are XOR-swizzled by the row index, so both the stage
+//     writes and the MFMA fragment reads hit 8 distinct bank groups per 8
+//     lanes (conflict-free).
+//   * B (weights, prepared layout): a column tile's chunk is one contiguous
+//     9 KB slab, so a workgroup streams a single sequential region; per chunk
+//     and column block each lane loads one 16-byte span (1 KB per wave-load)
+//     and one dword of four E4M3 scales, by buffer loads with scalar chunk
+//     offsets. Loads run five
+//     chunks ahead in a register ring (about 11 KB in flight per wave, which
+//     the HBM latency under load needs); decoding happens in registers straight
+//     into MFMA operand order, and every decoded B fragment feeds both row
+//     blocks.
 //   * The MFMA k-step of 16 is exactly one NVFP4 block; FP32 accumulation.
 // Epilogue: y = acc * fp32(g_row * alpha_e) (scales applied after
 // accumulation, never folded into decoded values), then
@@ -27,36 +34,40 @@
 //
 // Batch invariance: every output element is one chain of MFMAs over k in fixed
 // order whatever T, the tile or the other rows are; no split-K.
-// Block -> tile order: consecutive logical ids share an XCD (blockIdx % 8 picks
-// the XCD) and the M-tiles of one expert are adjacent, so a hot expert's weight
-// stream is fetched once into that XCD's L2 for all of its M-tiles.
+// Work order: the real work items (M-tile x column tile) are numbered
+// expert-major, then column tile, then M-tile, and each XCD (blockIdx % 8
+// picks it) takes one contiguous eighth of them. So the M-tiles that need the
+// same weight slab are dispatched together on one XCD and share it through
+// its L2 (a hot expert's weights are fetched once, not once per M-tile), and
+// an expert's activation rows stay in that L2 across its column tiles.
 #include "device.h"
 #include "kernels.h"
 
 namespace pmoe {
 
 constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 constexpr int kBlocksPerWave = 2;
-constexpr int kColTile = kWaves * kBlocksPerWave;  // column blocks per workgroup
+constexpr int kColTile = kColTileBlocks;            // column blocks per workgroup (4 waves x 2)
 constexpr int kStageK = 128;                       // reduction elements per LDS stage
-constexpr int kLdsRow = kStageK * 2 + 16;          // bytes per LDS A row (+16 pad)
-constexpr int kRing = 4;                           // B register ring slots per wave
+constexpr int kLdsRow = kStageK * 2;               // bytes per LDS A row (16 slots of 16 B)
+constexpr int kLdsStage = kTileM * kLdsRow;        // bytes per LDS stage buffer
+constexpr int kBufFlags = 0x00020000;              // raw buffer, 32-bit data format
+#ifndef PMOE_GEMM_RING
+#define PMOE_GEMM_RING 4
+#endif
+#ifndef PMOE_GEMM_WG_PER_CU
+#define PMOE_GEMM_WG_PER_CU 2
+#endif
+constexpr int kRing = PMOE_GEMM_RING;              // B register ring slots per wave (even)
+constexpr int kGroup = kRing / 2;                  // stages per loop iteration
+constexpr int kStages = (kGroup % 2) ? 3 : 2;      // LDS A stage buffers
 constexpr int kPrefetch = kRing - 1;               // B chunks in flight ahead of the one in use
 
-__host__ __device__ int fc_col_tiles(int NB) { return (NB + kColTile - 1) / kColTile; }
+__host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
 
 __device__ __forceinline__ _Float16 e4m3_to_half(uint32_t b) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false)[0];
-}
-
-// 4 x 8 codes of one row (16 bytes) with the scales of the 2 blocks they span
-// -> 32 FP16 values written to LDS as four 16-byte stores.
-__device__ __forceinline__ void decode_a_store(const uint4& q, uint32_t s2, uint8_t* dst) {
-  const _Float16 s0 = e4m3_to_half(s2 & 0xFFu), s1 = e4m3_to_half(s2 >> 8);
-  *reinterpret_cast<half8_t*>(dst + 0) = decode8(q.x, s0);
-  *reinterpret_cast<half8_t*>(dst + 16) = decode8(q.y, s0);
-  *reinterpret_cast<half8_t*>(dst + 32) = decode8(q.z, s1);
-  *reinterpret_cast<half8_t*>(dst + 48) = decode8(q.w, s1);
 }
 
 // Main loop + epilogue for one tile. TWO: the tile has more than 32 rows, so
@@ -65,36 +76,83 @@ __device__ __forceinline__ void decode_a_store(const uint4& q, uint32_t s2, uint
 // data is never used), which keeps the in-order load counters exact so the
 // four-chunk B ring really stays in flight.
 template <int MODE, bool TWO>
-__device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kTileM * kLdsRow],
+__device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
                                         int mrows, int nt) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps descriptors in SGPRs
   const int NB = P.NB, KC = P.KC;
 
-  // A loader: thread -> (row am, 32-element quarter aq) of each 128-element stage.
-  const int am = tid >> 2, aq = tid & 3;
-  const long a_row_bytes = (long)KC * 32;
-  const uint8_t* a_code = P.a_codes + (long)a_row[am] * a_row_bytes;
-  const uint8_t* a_scl = P.a_sf + (long)a_row[am] * (KC * 4);
-  uint8_t* a_dst0 = &a_lds[0][am * kLdsRow + aq * 64];
-  uint8_t* a_dst1 = &a_lds[1][am * kLdsRow + aq * 64];
-  // Stage s of this thread covers chunk 2s + aq/2; past the last chunk (the
-  // empty half of an odd final stage) it re-reads the last chunk instead.
-  auto a_load = [&](int s, uint4& q, uint32_t& sc) {
-    const int c = min(2 * s + (aq >> 1), KC - 1);
-    const int part = aq & 1;
-    q = *reinterpret_cast<const uint4*>(a_code + c * 32 + part * 16);
-    sc = *reinterpret_cast<const uint16_t*>(a_scl + c * 4 + part * 2);
+  // A stage fill: thread t -> row r = t/4 of the stage, elements 32*(t%4) ..
+  // +32 (k-chunks kk = 4*(t%4) + i), stored at slots kk ^ (r % 16). Rows of a
+  // skipped upper block are not filled (t >= 128 when !TWO). Out-of-range
+  // buffer reads (the empty half of an odd final stage at the last row)
+  // return zeros and are never used.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int ar = tid >> 2, aq = tid & 3;
+  const bool a_fill = TWO || ar < 32;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)P.a_codes, (short)0, (int)(P.a_rows * KC * 32), kBufFlags);
+  const __amdgpu_buffer_rsrc_t a_srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)P.a_sf, (short)0, (int)(P.a_rows * KC * 4), kBufFlags);
+  const uint32_t a_voff = (uint32_t)a_row[ar] * (uint32_t)(KC * 32) + aq * 16;
+  const uint32_t a_svoff = (uint32_t)a_row[ar] * (uint32_t)(KC * 4) + aq * 2;
+  int a_loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_loff[i] = ar * kLdsRow + (((4 * aq + i) ^ (ar & 15)) << 4);
+  struct ARaw {
+    u32x4 q;
+    uint32_t s;
   };
+  auto a_copy_load = [&](int st, ARaw& v) {
+    if (a_fill) {
+      v.q = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff, st * 64, 0);
+      v.s = __builtin_amdgcn_raw_buffer_load_b16(a_srsrc, a_svoff, st * 8, 0);
+    }
+  };
+  auto a_copy_store = [&](uint8_t* buf, const ARaw& v) {
+    if (a_fill) {
+      const half2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.s, 1.0f, false);
+      *reinterpret_cast<half8_t*>(buf + a_loff[0]) = decode8(v.q.x, sc[0]);
+      *reinterpret_cast<half8_t*>(buf + a_loff[1]) = decode8(v.q.y, sc[0]);
+      *reinterpret_cast<half8_t*>(buf + a_loff[2]) = decode8(v.q.z, sc[1]);
+      *reinterpret_cast<half8_t*>(buf + a_loff[3]) = decode8(v.q.w, sc[1]);
+    }
+  };
+  // MFMA fragment reads: lane -> row lane%32 (+32 for the upper block), k-chunk
+  // kk = 8*half + 2*j + lane/32 of the stage, at slot kk ^ row%16.
+  int frag[2][4];
+  {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) frag[hf][j] = r * kLdsRow + (((8 * hf + 2 * j + h) ^ (r & 15)) << 4);
+  }
 
-  const int frag_off = (lane & 31) * kLdsRow + (lane >> 5) * 16;
-
+  // B stream of this column tile: chunk c of its 16 column blocks is one
+  // contiguous 18 KB slab (16 KB codes + 2 KB scales); wave w reads blocks 2w
+  // and 2w+1 of it. Reads past the last chunk are out of the buffer range and
+  // return zeros. Column blocks past NB (padding of the last tile) hold zeros.
+  const int NT = padded_col_blocks(NB) / kColTileBlocks;
   const int p0 = nt * kColTile + wave * kBlocksPerWave;
-  const int q0 = min(p0, NB - 1), q1 = min(p0 + 1, NB - 1);
-  const uint4* bq0 = reinterpret_cast<const uint4*>(P.w_codes + ((long)e * NB + q0) * KC * 1024) + lane;
-  const uint4* bq1 = reinterpret_cast<const uint4*>(P.w_codes + ((long)e * NB + q1) * KC * 1024) + lane;
-  const uint32_t* bs0 = reinterpret_cast<const uint32_t*>(P.w_scales + ((long)e * NB + q0) * KC * 128) + (lane & 31);
-  const uint32_t* bs1 = reinterpret_cast<const uint32_t*>(P.w_scales + ((long)e * NB + q1) * KC * 128) + (lane & 31);
+  const long tile = (long)e * NT + nt;
+  const __amdgpu_buffer_rsrc_t bq = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(P.w_codes + tile * KC * (kColTileBlocks * 1024)), (short)0, KC * kColTileBlocks * 1024,
+      kBufFlags);
+  const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(P.w_scales + tile * KC * (kColTileBlocks * 128)), (short)0, KC * kColTileBlocks * 128,
+      kBufFlags);
+  const int pos0 = wave * kBlocksPerWave;
+  const int bq_voff0 = pos0 * 1024 + lane * 16, bq_voff1 = bq_voff0 + 1024;
+  const int bs_voff0 = pos0 * 128 + (lane & 31) * 4, bs_voff1 = bs_voff0 + 128;
+  auto load_q = [&](int voff, int c) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bq, voff, c * (kColTileBlocks * 1024), 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+  auto load_s = [&](int voff, int c) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bs, voff, c * (kColTileBlocks * 128), 0);
+  };
 
   floatx16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};  // [row block][col block]
 
@@ -106,17 +164,15 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kTil
   uint32_t rs0[kRing], rs1[kRing];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
-    const int c = min(i, KC - 1);
-    rq0[i] = bq0[c * 64];
-    rq1[i] = bq1[c * 64];
-    rs0[i] = bs0[c * 32];
-    rs1[i] = bs1[c * 32];
+    rq0[i] = load_q(bq_voff0, i);
+    rq1[i] = load_q(bq_voff1, i);
+    rs0[i] = load_s(bs_voff0, i);
+    rs1[i] = load_s(bs_voff1, i);
   }
   {
-    uint4 q;
-    uint32_t sc;
-    a_load(0, q, sc);
-    decode_a_store(q, sc, a_dst0);
+    ARaw v;
+    a_copy_load(0, v);
+    a_copy_store(&a_lds[0][0], v);
   }
   __syncthreads();
 
@@ -124,21 +180,21 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kTil
     // Refill the slot freed by chunk c - 1 before decoding slot i; the
     // scheduling barrier keeps these loads ahead of the decode.
     const int r = (i + kPrefetch) % kRing;
-    const int cn = min(c + kPrefetch, KC - 1);
-    rq0[r] = bq0[cn * 64];
-    rq1[r] = bq1[cn * 64];
-    rs0[r] = bs0[cn * 32];
-    rs1[r] = bs1[cn * 32];
+    const int cn = c + kPrefetch;
+    rq0[r] = load_q(bq_voff0, cn);
+    rq1[r] = load_q(bq_voff1, cn);
+    rs0[r] = load_s(bs_voff0, cn);
+    rs1[r] = load_s(bs_voff1, cn);
     __builtin_amdgcn_sched_barrier(0);
     const uint4 q0 = rq0[i], q1 = rq1[i];
     const uint32_t sc0 = rs0[i], sc1 = rs1[i];
-    const uint8_t* ab = abuf + frag_off + half * 128;
     half8_t a0[4], a1[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a0[j] = *reinterpret_cast<const half8_t*>(ab + 32 * j);
+    for (int j = 0; j < 4; ++j) a0[j] = *reinterpret_cast<const half8_t*>(abuf + frag[half][j]);
     if constexpr (TWO) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a1[j] = *reinterpret_cast<const half8_t*>(ab + 32 * kLdsRow + 32 * j);
+      for (int j = 0; j < 4; ++j)
+        a1[j] = *reinterpret_cast<const half8_t*>(abuf + 32 * kLdsRow + frag[half][j]);
     }
     {
       half2_t s01, s23;
@@ -175,36 +231,36 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kTil
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Full stage st (two chunks) in LDS buffer st & 1 == t, ring slots 2t, 2t+1;
-  // loads the next stage's A and decodes it into the other buffer.
-  auto stage = [&](const int st, const int t) {
-    uint4 qn;
-    uint32_t scn;
-    a_load(st + 1, qn, scn);  // clamped past the end; the last stage's copy is unused
+  // Full stage st (two chunks) in LDS buffer st % 3 == t, ring slots slot and
+  // slot + 1; loads the next stage's A and stores it into the next buffer.
+  auto stage = [&](const int st, const int t, const int slot) {
+    ARaw v;
+    a_copy_load(st + 1, v);  // past the end on the last stage; that copy is unused
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* abuf = t ? &a_lds[1][0] : &a_lds[0][0];
-    chunk(2 * st, abuf, 0, 2 * t);
-    chunk(2 * st + 1, abuf, 1, 2 * t + 1);
-    decode_a_store(qn, scn, t ? a_dst0 : a_dst1);
+    const uint8_t* abuf = &a_lds[t][0];
+    chunk(2 * st, abuf, 0, slot);
+    chunk(2 * st + 1, abuf, 1, slot + 1);
+    a_copy_store(&a_lds[(t + 1) % kStages][0], v);
     __syncthreads();
   };
 
+  // The loop body covers kGroup stages (kRing chunks): stage j of a group uses
+  // LDS buffer j % kStages and ring slots 2j, 2j+1, so every index is a
+  // compile-time constant after unrolling.
   const int nfull = KC >> 1;  // stages holding two chunks
   int st = 0;
-  for (; st + 2 <= nfull; st += 2) {
-    stage(st, 0);
-    stage(st + 1, 1);
+  for (; st + kGroup <= nfull; st += kGroup) {
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) stage(st + j, j % kStages, 2 * j);
   }
-  if (st < nfull) {  // one more full stage (st even: buffer 0, slots 0 and 1)
-    stage(st, 0);
-    ++st;
-  }
-  if (KC & 1) {  // final half stage: chunk KC-1 = 2*st, buffer st & 1, slot (2*st) % 4
-    const uint8_t* abuf = (st & 1) ? &a_lds[1][0] : &a_lds[0][0];
-    if (st & 1)
-      chunk(2 * st, abuf, 0, 2);
-    else
-      chunk(2 * st, abuf, 0, 0);
+  const int rem = nfull - st;  // remaining full stages, fewer than kGroup
+#pragma unroll
+  for (int j = 0; j < kGroup - 1; ++j)
+    if (j < rem) stage(st + j, j % kStages, 2 * j);
+  if (KC & 1) {  // final half stage: chunk KC-1 = 2*nfull, group position rem
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+      if (j == rem) chunk(2 * nfull, &a_lds[j % kStages][0], 0, 2 * j);
   }
 
   // ------------------------------------------------------------------ epilogue
@@ -248,20 +304,29 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kTil
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void fc_kernel(FcParams P) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM * kLdsRow];
+__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
   __shared__ float s_row[kTileM];
 
   const int tid = threadIdx.x;
-  const int per = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  // Work item -> (tile, column tile): items are numbered expert-major, then
+  // column tile, then M-tile; XCD x = blockIdx % 8 takes items
+  // [x*per, (x+1)*per) in order.
   const int NT = fc_col_tiles(P.NB);
-  const int nt = logical / P.max_tiles;
-  const int tile = logical - nt * P.max_tiles;
-  if (nt >= NT || tile >= P.counters[1]) return;
-  const int e = P.tiles[2 * tile];
-  const int row0 = P.expert_offsets[e] + P.tiles[2 * tile + 1];
+  const int total = P.counters[1] * NT;
+  const int per = (total + 7) >> 3;
+  const int j = blockIdx.x >> 3;
+  if (j >= per) return;
+  const int item = (blockIdx.x & 7) * per + j;
+  if (item >= total) return;
+  const int4 ta = reinterpret_cast<const int4*>(P.tiles)[item / NT];  // a tile of the item's expert
+  const int first = ta.z, count = ta.w;
+  const int local = item - first * NT;
+  const int nt = local / count;
+  const int4 td = reinterpret_cast<const int4*>(P.tiles)[first + (local - nt * count)];
+  const int e = td.x;
+  const int row0 = P.expert_offsets[e] + td.y;
   const int mrows = min(kTileM, P.expert_offsets[e + 1] - row0);
 
   if (tid < kTileM) {
@@ -281,9 +346,9 @@ hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s) {
   const long blocks = (long)p.max_tiles * fc_col_tiles(p.NB);
   const long grid = (blocks + 7) / 8 * 8;
   switch (mode) {
-    case kFc1Relu2: fc_kernel<kFc1Relu2><<<grid, 256, 0, s>>>(p); break;
-    case kFc1Swiglu: fc_kernel<kFc1Swiglu><<<grid, 256, 0, s>>>(p); break;
-    case kFc2: fc_kernel<kFc2><<<grid, 256, 0, s>>>(p); break;
+    case kFc1Relu2: fc_kernel<kFc1Relu2><<<grid, kThreads, 0, s>>>(p); break;
+    case kFc1Swiglu: fc_kernel<kFc1Swiglu><<<grid, kThreads, 0, s>>>(p); break;
+    case kFc2: fc_kernel<kFc2><<<grid, kThreads, 0, s>>>(p); break;
   }
   return hipGetLastError();
 }

@@ -9,8 +9,14 @@ namespace pmoe {
 constexpr int kTileM = 64;     // rows per M-tile of the grouped GEMMs (two MFMA row blocks)
 constexpr int kColBlock = 32;  // weight rows per prepared column block
 constexpr int kChunk = 64;     // reduction elements per prepared chunk
+constexpr int kColTileBlocks = 8;  // column blocks per column tile (one GEMM workgroup)
+__host__ __device__ inline int padded_col_blocks(int NB) {
+  return (NB + kColTileBlocks - 1) / kColTileBlocks * kColTileBlocks;
+}
 constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxBlocksPerThread = 4;  // per-row quantizer: rows up to 256*4*16 = 16384 elements
+constexpr int kMaxRow = 256 * kMaxBlocksPerThread * 16;
 
 // ---------------------------------------------------------------- quantizers
 hipError_t launch_quantize_bf16(const void* x, int T, int H, uint8_t* xq, uint8_t* x_sf,
@@ -28,7 +34,7 @@ struct RouteBuffers {
   int* rank_local;      // [TK]
   int* block_counts;    // [route blocks][E]
   int* expert_offsets;  // [E+1]
-  int* tiles;           // [max_tiles][2] = {expert, first local row}
+  int* tiles;           // [max_tiles][4] = {expert, first local row, expert's first tile, expert's tiles}
   int* counters;        // [4] = {R, tiles, 0, 0}
   int* row_of_route;    // [TK]
   int* route_of_row;    // [TK]
@@ -41,8 +47,9 @@ hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_o
 enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2 };
 
 struct FcParams {
-  const uint8_t* a_codes;    // A rows of Kd/2 bytes
-  const uint8_t* a_sf;       // A rows of Kd/16 bytes
+  const uint8_t* a_codes;    // A rows of Kd/2 bytes (packed E2M1)
+  const uint8_t* a_sf;       // A rows of Kd/16 bytes (E4M3 block scales)
+  long a_rows;               // rows in the A buffers (codes < 4 GiB)
   const float* a_scale;      // per A row
   const int* route_of_row;   // FC1: expert-sorted row -> route (A row = route / topk); FC2: null
   int topk;
@@ -51,9 +58,9 @@ struct FcParams {
   const float* w_alpha;
   int NB;                    // column blocks of 32 in this FC
   int KC;                    // chunks of 64 along the reduction
-  const int* tiles;
+  const int* tiles;          // [tiles][4], see RouteBuffers
   const int* expert_offsets;
-  const int* counters;
+  const int* counters;       // [1] = number of M-tiles
   int max_tiles;
   void* out;                 // FC1: float h [rows][out_stride]; FC2: BF16 z [rows][out_stride]
   int out_stride;

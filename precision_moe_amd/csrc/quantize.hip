@@ -2,11 +2,12 @@
 // the requantizer of the FP32 expert intermediate (FP32 rows)
 // [Megatron-LM #8262 . Background; What is added; How to extend].
 //
-// One wave per row. Pass 1 reads the row once for its absolute maximum
-// (wave-reduced; max is exact and order-free), pass 2 re-reads it (now in
-// cache) and quantizes 16-element blocks, lane b handling blocks b, b+64, ...
-// so every load and store of a wave is one contiguous span. HBM bound: a BF16
-// row of H elements moves 2H bytes in and 9H/16 bytes out.
+// One 256-thread workgroup per row, single pass: thread t owns 16-element
+// blocks t, t+256, ... (at most kMaxBlocksPerThread), keeps them in registers,
+// reduces the row's absolute maximum across the workgroup (max is exact and
+// order-free), then quantizes its blocks. Loads and stores of a wave are
+// contiguous spans. HBM bound: a BF16 row of H elements moves 2H bytes in and
+// 9H/16 out; an FP32 row 4L in and 9L/16 out.
 #include "device.h"
 #include "kernels.h"
 
@@ -44,46 +45,54 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
                                                             int L, uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float red[4];
+  const long row = blockIdx.x;
   const int nrows = rows_dev ? *rows_dev : rows;
   if (row >= nrows) return;
+  const int tid = threadIdx.x;
   const int nblk = L / kBlock;
   const void* xr = kBf16 ? (const void*)(static_cast<const uint16_t*>(x) + row * L)
                          : (const void*)(static_cast<const float*>(x) + row * L);
+  float v[kMaxBlocksPerThread][16];
   float amax = 0.0f;
-  for (int b = lane; b < nblk; b += 64) {
-    float v[16];
-    load_block16<kBf16>(xr, b, v);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  for (int i = 0; i < kMaxBlocksPerThread; ++i) {
+    const int b = tid + 256 * i;
+    if (b < nblk) {
+      load_block16<kBf16>(xr, b, v[i]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][k]));
+    }
   }
   amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
   const float g = amax * kRecipeConst;
   uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
   uint8_t* sr = sf + row * nblk;
-  for (int b = lane; b < nblk; b += 64) {
-    float v[16];
-    load_block16<kBf16>(xr, b, v);
-    uint32_t lo, hi;
-    uint32_t s = quant_block16(v, g, lo, hi);
-    qr[b] = make_uint2(lo, hi);
-    sr[b] = (uint8_t)s;
+#pragma unroll
+  for (int i = 0; i < kMaxBlocksPerThread; ++i) {
+    const int b = tid + 256 * i;
+    if (b < nblk) {
+      uint32_t lo, hi;
+      const uint32_t s = quant_block16(v[i], g, lo, hi);
+      qr[b] = make_uint2(lo, hi);
+      sr[b] = (uint8_t)s;
+    }
   }
-  if (lane == 0) scale[row] = g;
+  if (tid == 0) scale[row] = g;
 }
 
 hipError_t launch_quantize_bf16(const void* x, int T, int H, uint8_t* xq, uint8_t* x_sf,
                                 float* x_scale, hipStream_t s) {
-  dim3 grid((T + 3) / 4);
-  quantize_rows_kernel<true><<<grid, 256, 0, s>>>(x, T, nullptr, H, xq, x_sf, x_scale);
+  quantize_rows_kernel<true><<<T, 256, 0, s>>>(x, T, nullptr, H, xq, x_sf, x_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L, uint8_t* hq,
                                uint8_t* h_sf, float* h_scale, hipStream_t s) {
-  dim3 grid((R + 3) / 4);
-  quantize_rows_kernel<false><<<grid, 256, 0, s>>>(h, R, rows_dev, L, hq, h_sf, h_scale);
+  quantize_rows_kernel<false><<<R, 256, 0, s>>>(h, R, rows_dev, L, hq, h_sf, h_scale);
   return hipGetLastError();
 }
 

@@ -11,7 +11,9 @@
 //                   per-expert counts.
 //   route_scan    : one workgroup: per expert, exclusive prefix over blocks
 //                   (in place), totals, exclusive scan over experts, and the
-//                   M-tile list {expert, first local row} (tiles of 32 rows).
+//                   M-tile list {expert, first local row, expert's first
+//                   tile, expert's tile count} (tiles of 64 rows, grouped by
+//                   expert in expert order).
 //   route_scatter : row = expert start + block prefix + in-block rank;
 //                   writes row_of_route and route_of_row.
 // A route is valid iff expert_offset <= id < expert_offset + E; other ids
@@ -101,8 +103,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ bloc
   if (e < E) {
     expert_offsets[e] = start;
     for (int i = 0; i < ntiles; ++i) {
-      tiles[2 * (tstart + i)] = e;
-      tiles[2 * (tstart + i) + 1] = i * kTileM;
+      int4* t = reinterpret_cast<int4*>(tiles) + tstart + i;
+      *t = make_int4(e, i * kTileM, tstart, ntiles);
     }
   }
   if (e == 0) {

@@ -4,7 +4,9 @@
 // Two kernels per FC matrix:
 //   1. amax partials: each workgroup reduces max|w| over a 64K-element span of
 //      one expert (exact and order-free, so the result is deterministic);
-//   2. quantize: each workgroup owns one 32-row column block of one expert,
+//   2. quantize: each workgroup owns one 32-row column block of one expert
+//      (column blocks past N, which pad the last 8-block column tile, are
+//      written as zeros),
 //      folds its expert's partials into amax, derives
 //        w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale)
 //      and quantizes every 16-block of its rows with g = alpha, writing codes
@@ -46,9 +48,10 @@ __global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __rest
         __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
-// grid (NB, E). gated_I > 0 selects the gate/up interleave of a gated FC1.
+// grid (NBp, E) with NBp = NB rounded up to a multiple of 8. gated_I > 0
+// selects the gate/up interleave of a gated FC1.
 __global__ __launch_bounds__(256) void weight_quant_kernel(
-    const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int KC,
+    const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int NBp, int KC,
     const float* __restrict__ partials, int parts, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ alpha_out) {
   const int p = blockIdx.x, e = blockIdx.y;
@@ -64,30 +67,35 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   if (p == 0 && threadIdx.x == 0) alpha_out[e] = alpha;
 
   const int nkb = Kd / kBlock;
-  const long chunk_base = ((long)e * NB + p) * KC;
+  // chunk c of column block p sits at slab ((e*NT + p/8)*KC + c)*8 + p%8
+  const long tile_base = ((long)e * (NBp / kColTileBlocks) + p / kColTileBlocks) * KC;
+  const int pos = p % kColTileBlocks;
   for (int idx = threadIdx.x; idx < kColBlock * nkb; idx += 256) {
     const int col = idx / nkb, kb = idx - col * nkb;
-    int n;
+    int n;  // canonical row (only read when p < NB)
     if (gated_I > 0)
       n = ((p & 1) ? gated_I : 0) + kColBlock * (p >> 1) + col;
     else
       n = kColBlock * p + col;
-    const uint4* src = reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + kb * kBlock);
-    uint4 u0 = src[0], u1 = src[1];
-    uint32_t v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    float x[16];
+    uint32_t lo = 0, hi = 0, sf = 0;
+    if (p < NB) {
+      const uint4* src = reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + kb * kBlock);
+      uint4 u0 = src[0], u1 = src[1];
+      uint32_t v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float x[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
-      x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+      for (int i = 0; i < 8; ++i) {
+        x[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+        x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+      }
+      sf = quant_block16(x, alpha, lo, hi);
     }
-    uint32_t lo, hi;
-    const uint32_t sf = quant_block16(x, alpha, lo, hi);
     const int c = kb >> 2, j = kb & 3;
-    uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + ((chunk_base + c) * 64) * 16);
+    const long slab = (tile_base + c) * kColTileBlocks + pos;
+    uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + slab * 1024);
     cdst[col * 4 + j] = lo;         // lane col (elements 0..7 of the block)
     cdst[(col + 32) * 4 + j] = hi;  // lane col + 32 (elements 8..15)
-    scales[((chunk_base + c) * 32 + col) * 4 + j] = (uint8_t)sf;
+    scales[slab * 128 + col * 4 + j] = (uint8_t)sf;
   }
 }
 
@@ -99,8 +107,9 @@ hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int NB = N / kColBlock, KC = Kd / kChunk;
-  weight_quant_kernel<<<dim3(NB, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, KC, partials, parts, codes,
-                                                  scales, alpha);
+  const int NBp = padded_col_blocks(NB);
+  weight_quant_kernel<<<dim3(NBp, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, NBp, KC, partials, parts,
+                                                   codes, scales, alpha);
   return hipGetLastError();
 }
 

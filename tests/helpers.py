@@ -6,6 +6,8 @@ inverts it so prepared bytes can be compared with the oracle's canonical
 """
 import numpy as np
 
+TILE = 8  # column blocks (of 32 rows) per column tile of the prepared layout
+
 
 def prepared_row_map(N, gated_I):
     """Canonical row index of each prepared row p*32 + col."""
@@ -17,12 +19,17 @@ def prepared_row_map(N, gated_I):
     return 32 * p + col
 
 
-def canonical_from_prepared(codes, scales, E, N, Kd, gated_I=0):
+def canonical_from_prepared(codes, scales, E, N, Kd, gated_I=0, check_padding=True):
     NB, KC = N // 32, Kd // 64
-    c = np.asarray(codes, np.uint8).reshape(E, NB, KC, 2, 32, 4, 4)      # e p c h col j b
-    c = c.transpose(0, 1, 4, 2, 5, 3, 6).reshape(E, NB * 32, KC * 32)     # e (p col) (c j h b)
-    s = np.asarray(scales, np.uint8).reshape(E, NB, KC, 32, 4)            # e p c col j
-    s = s.transpose(0, 1, 3, 2, 4).reshape(E, NB * 32, KC * 4)
+    NBp = -(-NB // TILE) * TILE
+    NT = NBp // TILE
+    c = np.asarray(codes, np.uint8).reshape(E, NT, KC, TILE, 2, 32, 4, 4)  # e ct c pos h col j b
+    c = c.transpose(0, 1, 3, 5, 2, 6, 4, 7).reshape(E, NBp * 32, KC * 32)  # e (ct pos col) (c j h b)
+    s = np.asarray(scales, np.uint8).reshape(E, NT, KC, TILE, 32, 4)       # e ct c pos col j
+    s = s.transpose(0, 1, 3, 4, 2, 5).reshape(E, NBp * 32, KC * 4)
+    if check_padding:
+        assert not c[:, NB * 32:].any() and not s[:, NB * 32:].any(), "padding blocks must be zero"
+    c, s = c[:, :NB * 32], s[:, :NB * 32]
     rows = prepared_row_map(N, gated_I)
     cq = np.empty_like(c)
     cs = np.empty_like(s)

@@ -43,9 +43,14 @@ def test_binding_constants_match_header():
 
 def test_version_and_sizes():
     assert pm.lib().pmoe_version() >= 100
-    E, H, I = 4, 256, 128
+    E, H, I = 4, 1024, 512
     assert pm.weight_bytes(E, 2 * I, H, I) == (E * 2 * I * H // 2, E * 2 * I * H // 16, E * H * I // 2,
                                               E * H * I // 16)
+    # rows are padded to whole column tiles of 8 blocks x 32 rows
+    pad = lambda n: -(-n // 256) * 256
+    E, H, I = 3, 320, 192
+    assert pm.weight_bytes(E, I, H, I) == (E * pad(I) * H // 2, E * pad(I) * H // 16, E * pad(H) * I // 2,
+                                          E * pad(H) * I // 16)
     assert pm.lib().pmoe_prepare_workspace_bytes(E, I, H, I) > 0
 
 

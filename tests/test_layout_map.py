@@ -3,20 +3,22 @@ element-by-element construction from the layout's definition in include/pmoe.h."
 import numpy as np
 import pytest
 
-from helpers import canonical_from_prepared, prepared_row_map
+from helpers import TILE, canonical_from_prepared, prepared_row_map
 
 
-@pytest.mark.parametrize("gated", [False, True])
-def test_inverse_layout_map(gated):
+@pytest.mark.parametrize("gated,I", [(False, 64), (True, 64), (False, 640), (True, 320)])
+def test_inverse_layout_map(gated, I):
     rng = np.random.default_rng(0)
-    E, I, H = 2, 64, 128
+    E, H = 2, 128
     gI = I if gated else 0
     N = 2 * I if gated else I
     canon = rng.integers(0, 256, (E, N, H // 2), dtype=np.uint8)
     canon_s = rng.integers(0, 127, (E, N, H // 16), dtype=np.uint8)
     NB, KC = N // 32, H // 64
-    prep = np.zeros(E * N * H // 2, np.uint8)
-    prep_s = np.zeros(E * N * H // 16, np.uint8)
+    NBp = -(-NB // TILE) * TILE
+    NT = NBp // TILE
+    prep = np.zeros(E * NBp * 32 * H // 2, np.uint8)
+    prep_s = np.zeros(E * NBp * 32 * H // 16, np.uint8)
     rows = prepared_row_map(N, gI)
     for e in range(E):
         for p in range(NB):
@@ -30,9 +32,11 @@ def test_inverse_layout_map(gated):
                             for i in range(8):
                                 k = c * 64 + 16 * j + 8 * h + i
                                 nib = (canon[e, n, k // 2] >> (4 * (k % 2))) & 15
-                                off = (((e * NB + p) * KC + c) * 64 + col + 32 * h) * 16 + j * 4 + i // 2
+                                slab = ((e * NT + p // TILE) * KC + c) * TILE + p % TILE
+                                off = (slab * 64 + col + 32 * h) * 16 + j * 4 + i // 2
                                 prep[off] |= nib << (4 * (i % 2))
                     for j in range(4):
-                        prep_s[(((e * NB + p) * KC + c) * 32 + col) * 4 + j] = canon_s[e, n, c * 4 + j]
+                        slab = ((e * NT + p // TILE) * KC + c) * TILE + p % TILE
+                        prep_s[(slab * 32 + col) * 4 + j] = canon_s[e, n, c * 4 + j]
     cq, cs = canonical_from_prepared(prep, prep_s, E, N, H, gI)
     assert np.array_equal(cq, canon) and np.array_equal(cs, canon_s)
