@@ -13,7 +13,8 @@ H=7168, I=3072, SwiGLU, top-6, T=1024 tokens, two hot experts (router logits
 Prints one JSON line. `roofline` is the dominant kernel (FC1 grouped GEMM):
 algorithmic bytes per launch over its average duration, measured here with
 HIP events around that step on the stream it runs on. `cpu_baseline` times
-the CPU oracle on a bounded sample (all routes of two experts).
+the CPU oracle on a bounded sample (all routes of the first --cpu-experts
+experts).
 """
 import argparse
 import json
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="ep4_t1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--cpu-experts", type=int, default=20,
+                    help="the CPU oracle baseline runs all routes of this many experts")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(calibrates the HBM byte counters) and exit")
@@ -69,8 +72,8 @@ def algorithmic_bytes(w, counts, T, R):
     }
 
 
-def cpu_baseline(w, ids, wts):
-    """Oracle throughput on all routes of two experts (one hot, one ordinary)."""
+def cpu_baseline(w, ids, wts, n_experts):
+    """Oracle throughput on all routes of the first n_experts experts (expert 0 is hot)."""
     import synth
     from oracle import moe as om
     from oracle import quant as oq
@@ -79,7 +82,7 @@ def cpu_baseline(w, ids, wts):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    experts = [0, 1]
+    experts = list(range(n_experts))
     W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
     for e in experts:
         W.expert(e)                                   # preparation is outside the timed region
@@ -105,6 +108,7 @@ def main():
 
     import torch
     import precision_moe_amd as pm
+    from precision_moe_amd import profiling
     import synth
 
     if args.copy_bytes:
@@ -162,15 +166,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The step is issued as three calls so that HIP events on the launch stream
+    # bracket the FC1 kernel inside the timed region (an event costs ~nothing on
+    # the GPU); the roofline figure uses their average.
+    def timed_step(ev_a, ev_b):
+        pm.quantize_input_per_token(x, out=(xq, xs, xg))
+        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_ROUTE, pm.STEP_ROUTE))
+        ev_a.record()
+        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_FC1, pm.STEP_FC1))
+        ev_b.record()
+        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_REQUANT, pm.STEP_FINALIZE))
+
+    fc1_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        timed_step(*fc1_evs[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    fc1_ms_timed = float(np.mean([a.elapsed_time(b) for a, b in fc1_evs]))
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
 
     # ---------------------------------------------------------------- per-step events
@@ -199,7 +217,8 @@ def main():
     fc1_flops = 2.0 * R * w.N1 * w.H
     kernels["fc1"]["TFLOP/s"] = float(fc1_flops / (stage_ms[2] * 1e-3) / 1e12)
     kernels["fc2"]["TFLOP/s"] = float(2.0 * R * w.H * w.I / (stage_ms[4] * 1e-3) / 1e12)
-    fc1_gbs = kernels["fc1"]["GB/s"]
+    fc1_gbs = ab["fc1"] / (fc1_ms_timed * 1e-3) / 1e9
+    traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", f"fc1_{w.name}_hbm_traffic.txt"), w.name)
 
     result = {
         "metric": METRIC,
@@ -222,13 +241,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "fc1 grouped GEMM (SwiGLU epilogue)" if w.gated else
                      "fc1 grouped GEMM (squared-ReLU epilogue)",
                      "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3},
         "kernels": kernels,
         "prepare": prepare,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        result["cpu_baseline"] = cpu_baseline(w, ids_np, wts_np)
+        result["cpu_baseline"] = cpu_baseline(w, ids_np, wts_np, args.cpu_experts)
     print(json.dumps(result), flush=True)
 
 

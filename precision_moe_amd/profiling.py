@@ -1,0 +1,156 @@
+"""Summaries of rocprofv3 output for the pmoe kernels (short text files).
+
+    python -m precision_moe_amd.profiling stats <rocprofv3 csv dir> <workload> <out.txt> "<command>"
+        per-kernel call count and average / total duration from a
+        `rocprofv3 --kernel-trace --stats --output-format csv` run
+    python -m precision_moe_amd.profiling traffic <fetch dir> <write dir> <copy fetch dir>
+        <copy write dir> <copy bytes> <kernel substring> <workload> <out.txt> "<commands>"
+        HBM bytes per dispatch of one kernel from `--pmc FETCH_SIZE` and
+        `--pmc WRITE_SIZE` runs, each scaled by what the same counter reads for
+        a plain device copy of known size
+
+The traffic summary records a hash of the GEMM sources it was measured with;
+bench.py reports the figure only while the sources still match.
+"""
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gemm.hip", "device.h", "kernels.h")]
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(directory, pattern):
+    out = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", pattern), recursive=True)):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _col(row, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(names)
+
+
+def _short(name):
+    """Kernel name without its trailing parameter list (template arguments kept)."""
+    name = name.strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    return name.replace("void ", "").strip()
+
+
+def kernel_stats(directory):
+    """{kernel: (calls, avg_us, total_us)} from *kernel_stats.csv."""
+    res = {}
+    for r in _rows(directory, "*kernel_stats.csv"):
+        name = _col(r, "Name", "KernelName", "Kernel_Name")
+        calls = int(float(_col(r, "Calls")))
+        total = float(_col(r, "TotalDurationNs", "Total_Duration_Ns")) / 1e3
+        res[_short(name)] = (calls, total / max(calls, 1), total)
+    return res
+
+
+def counter_means(directory, counter):
+    """{kernel: mean counter value per dispatch} from *counter_collection.csv."""
+    acc = {}
+    for r in _rows(directory, "*counter_collection.csv"):
+        if _col(r, "Counter_Name") != counter:
+            continue
+        k = _short(_col(r, "Kernel_Name"))
+        acc.setdefault(k, []).append(float(_col(r, "Counter_Value")))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_stats(directory, workload, out, command):
+    st = kernel_stats(directory)
+    lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}",
+             "# kernel | calls | avg us | total us"]
+    pm = {k: v for k, v in st.items() if "pmoe" in k}
+    for k, (c, a, t) in sorted(pm.items(), key=lambda kv: -kv[1][2]):
+        lines.append(f"{k} | {c} | {a:.2f} | {t:.1f}")
+    other = [v for k, v in st.items() if "pmoe" not in k]
+    lines.append(f"(other kernels: input generation and setup) | {sum(c for c, _, _ in other)} | - | "
+                 f"{sum(t for _, _, t in other):.1f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, workload, out, command):
+    def one(d, counter):
+        vals = {k: v for k, v in counter_means(d, counter).items() if kernel in k}
+        if len(vals) != 1:
+            raise SystemExit(f"{counter}: expected one kernel matching {kernel!r}, got {list(vals)}")
+        return next(iter(vals.items()))
+    name, fetch = one(fetch_dir, "FETCH_SIZE")
+    _, write = one(write_dir, "WRITE_SIZE")
+    def copy_kernel(d, counter):
+        vals = counter_means(d, counter)
+        copies = [v for k, v in vals.items() if "copy" in k.lower()]
+        return max(copies or vals.values())
+    cf = copy_kernel(cf_dir, "FETCH_SIZE")
+    cw = copy_kernel(cw_dir, "WRITE_SIZE")
+    ff = copy_bytes / (cf * 1024.0)
+    wf = copy_bytes / (cw * 1024.0)
+    hbm = fetch * 1024 * ff + write * 1024 * wf
+    lines = [
+        f"# rocprofv3 HBM byte counters for {name}, workload {workload}",
+        f"# commands: {command}",
+        f"# calibration: a plain device copy of {copy_bytes} bytes reads FETCH_SIZE={cf:.1f} KiB "
+        f"(factor {ff:.4f}) and WRITE_SIZE={cw:.1f} KiB (factor {wf:.4f})",
+        f"kernel={name}",
+        f"workload={workload}",
+        f"source_sha256={gemm_source_hash()}",
+        f"fetch_kib_per_dispatch={fetch:.1f}",
+        f"write_kib_per_dispatch={write:.1f}",
+        f"fetch_factor={ff:.6f}",
+        f"write_factor={wf:.6f}",
+        f"hbm_bytes_per_dispatch={hbm:.0f}",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_traffic(path, workload):
+    """HBM bytes per dispatch from a traffic summary, or None if absent, for another
+    workload, or measured with different GEMM sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k] = v
+    if kv.get("workload") != workload or kv.get("source_sha256") != gemm_source_hash():
+        return None
+    return float(kv["hbm_bytes_per_dispatch"])
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1]
+    if cmd == "stats":
+        write_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif cmd == "traffic":
+        write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7],
+                      sys.argv[8], sys.argv[9], sys.argv[10])
+    else:
+        raise SystemExit(__doc__)
