@@ -8,6 +8,9 @@
         HBM bytes per dispatch of one kernel from `--pmc FETCH_SIZE` and
         `--pmc WRITE_SIZE` runs, each scaled by what the same counter reads for
         a plain device copy of known size
+    python -m precision_moe_amd.profiling table <trace dir> <fetch dir> <write dir> <copy fetch dir>
+        <copy write dir> <copy bytes> <mfma counter dir> <workload> <out.txt> "<commands>"
+        every pmoe kernel: HBM bytes and GB/s, MFMA instructions and busy fraction
 
 The traffic summary records a hash of the GEMM sources it was measured with;
 bench.py reports the figure only while the sources still match.
@@ -130,6 +133,45 @@ def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, work
         f.write("\n".join(lines) + "\n")
 
 
+def write_table(kt_dir, fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, mfma_dir, workload, out,
+                command):
+    """Per pmoe kernel: HBM bytes and GB/s from the byte counters over the trace's
+    average duration, and MFMA busy fraction from SQ_VALU_MFMA_BUSY_CYCLES."""
+    st = kernel_stats(kt_dir)
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+
+    def copy_kernel(d, counter):
+        vals = counter_means(d, counter)
+        copies = [v for k, v in vals.items() if "copy" in k.lower()]
+        return max(copies or vals.values())
+    ff = copy_bytes / (copy_kernel(cf_dir, "FETCH_SIZE") * 1024.0)
+    wf = copy_bytes / (copy_kernel(cw_dir, "WRITE_SIZE") * 1024.0)
+    busy = counter_means(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    insts = counter_means(mfma_dir, "SQ_INSTS_MFMA")
+    lines = [
+        f"# rocprofv3 per-kernel HBM bytes and MFMA utilisation, workload {workload}",
+        f"# commands: {command}",
+        f"# HBM bytes = FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {wf:.4f} (factors from a {copy_bytes}-byte "
+        "device copy); GB/s over the kernel trace's average duration",
+        "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (duration x 2.4 GHz x 1024 SIMDs): the share of the "
+        "nominal MFMA issue capacity; MFMA TFLOP/s = SQ_INSTS_MFMA x 32768 (32x32x16) / duration, "
+        "padded rows included",
+        "# kernel | avg us | read MB | write MB | HBM GB/s | MFMA insts | MFMA busy | MFMA TFLOP/s",
+    ]
+    for k, (calls, avg, _) in sorted(st.items(), key=lambda kv: -kv[1][2]):
+        if "pmoe" not in k or k not in fetch:
+            continue
+        rd = fetch[k] * 1024 * ff
+        wr = write.get(k, 0.0) * 1024 * wf
+        util = busy.get(k, 0.0) / (avg * 1e-6 * 2.4e9 * 1024)
+        tf = insts.get(k, 0.0) * 32768 / (avg * 1e-6) / 1e12
+        lines.append(f"{k} | {avg:.2f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / (avg * 1e3):.0f} | "
+                     f"{insts.get(k, 0.0):.4g} | {util:.3f} | {tf:.0f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(path, workload):
     """HBM bytes per dispatch from a traffic summary, or None if absent, for another
     workload, or measured with different GEMM sources."""
@@ -152,5 +194,7 @@ if __name__ == "__main__":
     elif cmd == "traffic":
         write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7],
                       sys.argv[8], sys.argv[9], sys.argv[10])
+    elif cmd == "table":
+        write_table(*sys.argv[2:7], int(sys.argv[7]), *sys.argv[8:12])
     else:
         raise SystemExit(__doc__)
