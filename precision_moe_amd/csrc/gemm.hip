@@ -21,11 +21,9 @@
 //     9 KB slab, so a workgroup streams a single sequential region; per chunk
 //     and column block each lane loads one 16-byte span (1 KB per wave-load)
 //     and one dword of four E4M3 scales, by buffer loads with scalar chunk
-//     offsets. Loads run five
-//     chunks ahead in a register ring (about 11 KB in flight per wave, which
-//     the HBM latency under load needs); decoding happens in registers straight
-//     into MFMA operand order, and every decoded B fragment feeds both row
-//     blocks.
+//     offsets. Loads run kRing - 1 chunks ahead in a register ring; decoding
+//     happens in registers straight into MFMA operand order, and every
+//     decoded B fragment feeds both row blocks.
 //   * The MFMA k-step of 16 is exactly one NVFP4 block; FP32 accumulation.
 // Epilogue: y = acc * fp32(g_row * alpha_e) (scales applied after
 // accumulation, never folded into decoded values), then
@@ -130,8 +128,8 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       for (int j = 0; j < 4; ++j) frag[hf][j] = r * kLdsRow + (((8 * hf + 2 * j + h) ^ (r & 15)) << 4);
   }
 
-  // B stream of this column tile: chunk c of its 16 column blocks is one
-  // contiguous 18 KB slab (16 KB codes + 2 KB scales); wave w reads blocks 2w
+  // B stream of this column tile: chunk c of its 8 column blocks is one
+  // contiguous 9 KB slab (8 KB codes + 1 KB scales); wave w reads blocks 2w
   // and 2w+1 of it. Reads past the last chunk are out of the buffer range and
   // return zeros. Column blocks past NB (padding of the last tile) hold zeros.
   const int NT = padded_col_blocks(NB) / kColTileBlocks;

@@ -12,24 +12,34 @@
         <copy write dir> <copy bytes> <mfma counter dir> <workload> <out.txt> "<commands>"
         every pmoe kernel: HBM bytes and GB/s, MFMA instructions and busy fraction
 
-The traffic summary records a hash of the GEMM sources it was measured with;
-bench.py reports the figure only while the sources still match.
+The traffic summary records a hash of the GEMM sources it was measured with
+(comments and whitespace excluded); bench.py reports the figure only while the
+sources still match.
 """
 import csv
 import glob
 import hashlib
 import os
+import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gemm.hip", "device.h", "kernels.h")]
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed: edits to
+    comments or layout do not change the kernel, so they do not change the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_source_hash():
     h = hashlib.sha256()
     for p in GEMM_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
