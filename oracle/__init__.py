@@ -21,6 +21,9 @@ Modules:
              quantizer, dequantizers.
   moe     -- gating detection, routing, FC1, activation, FC2, finalize, the
              whole pipeline, and two brute-force references used as pins.
+  recipes -- the per-tensor NVFP4 (static calibrated input scales folded into
+             the alphas) and weight-only W4A16 (BF16 activations) variants of
+             the pipeline [Megatron-LM #8262 . How to extend].
 
 Parity pins: every function here is pinned by a CPU test against something
 other than itself (hand enumerations, a library cast, brute force, closed
