@@ -130,6 +130,25 @@ int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, i
                          void* w2_codes, void* w2_scales, float* w2_alpha,
                          void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Preparation for the per-tensor NVFP4 recipe [Megatron-LM #8262 . How to
+ * extend, 'per_tensor']: codes and block scales exactly as pmoe_prepare_weights,
+ * with the static FC1 / FC2 input scales folded into the alphas:
+ *   w1_alpha[e] = fp32(1 / fp32(w_scale1[e] * a1)),
+ *   w2_alpha[e] = fp32(1 / fp32(w_scale2[e] * a2)).
+ *   a1_scale, a2_scale : device float32 scalars (4-byte aligned), read by the
+ *                        kernels, so the call never waits on the host. They
+ *                        use the weights' convention, a = 2688 / calibrated
+ *                        amax, and must be positive and finite (not checked:
+ *                        they live on the device).
+ * Other arguments, layout and errors as pmoe_prepare_weights.
+ */
+int pmoe_prepare_weights_per_tensor(const void* w1, const void* w2, int E, int N1, int H, int I,
+                                    const float* a1_scale, const float* a2_scale,
+                                    void* w1_codes, void* w1_scales, float* w1_alpha,
+                                    void* w2_codes, void* w2_scales, float* w2_alpha,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* ============================================================ activations */
 
 /*
@@ -148,6 +167,18 @@ int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, i
  */
 int pmoe_quantize_input_per_token(const void* x, int T, int H,
                                   void* xq, void* x_sf, float* x_scale, void* stream);
+
+/*
+ * NVFP4 quantization of BF16 activations with a static, calibrated scale
+ * (per-tensor recipe) [Megatron-LM #8262 . How to extend, 'per_tensor', row
+ * 'FC1 input']: every row uses g = fp32(1 / a1) in the block steps of
+ * pmoe_quantize_input_per_token; blocks beyond the scale's range saturate
+ * (scale 448, codes +-6). No per-token scale is produced.
+ *   a1_scale : device float32 scalar (a1 = 2688 / calibrated amax), positive and finite
+ *   xq, x_sf : as pmoe_quantize_input_per_token.
+ */
+int pmoe_quantize_input_per_tensor(const void* x, int T, int H, const float* a1_scale,
+                                   void* xq, void* x_sf, void* stream);
 
 /*
  * The same per-row NVFP4 quantizer applied to FP32 rows: the requantization of
@@ -170,10 +201,11 @@ size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act);
 #define PMOE_WS_ROUTE_OF_ROW 1   /* int32 [T*K]   route index of each row (first R valid)        */
 #define PMOE_WS_EXPERT_OFFSETS 2 /* int32 [E+1]   first row of each local expert; [E] = R          */
 #define PMOE_WS_COUNTERS 3       /* int32 [4]     {R, number of M-tiles, 0, 0}                     */
-#define PMOE_WS_H 4              /* float32 [T*K, I]   activation output (rows < R valid)          */
+#define PMOE_WS_H 4              /* float32 [T*K, I]   activation output (rows < R valid);
+                                    BF16 [T*K, I] under pmoe_routed_moe_w4a16                   */
 #define PMOE_WS_HQ 5             /* uint8 [T*K, I/2]   requantized intermediate codes              */
 #define PMOE_WS_H_SF 6           /* uint8 [T*K, I/16]  its E4M3 block scales                        */
-#define PMOE_WS_H_SCALE 7        /* float32 [T*K]      its per-row scales                           */
+#define PMOE_WS_H_SCALE 7        /* float32 [T*K]      its per-row scales (per-token recipe only)   */
 #define PMOE_WS_Z 8              /* BF16 [T*K, H]      per-route FC2 outputs                         */
 #define PMOE_WS_NUM_FIELDS 9
 
@@ -234,6 +266,44 @@ int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
 int pmoe_routed_moe_steps(int first, int last,
                           const void* xq, const void* x_sf, const float* x_scale,
                           const void* topk_ids, int ids_type, const float* topk_w,
+                          int T, int K, int E, int H, int I, int N1, int expert_offset,
+                          const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                          const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                          int act, void* ws, size_t ws_bytes, void* out, void* stream);
+
+/*
+ * The routed path under the per-tensor NVFP4 recipe [Megatron-LM #8262 . How
+ * to extend, 'per_tensor']. As pmoe_routed_moe, except:
+ *   xq, x_sf   : output of pmoe_quantize_input_per_tensor (no per-token scale)
+ *   weights    : output of pmoe_prepare_weights_per_tensor (folded alphas)
+ *   a2_scale   : device float32 scalar, the static FC2 input scale
+ *   y = fp32(sum_k dec(xq[t,k]) * dec(W1[e,:,k])) * alpha1'[e]
+ *   (hq, h_sf) = quantization of h with g = fp32(1 / a2) for every row
+ *   z = bf16(fp32(sum_k dec(hq) * dec(W2[e])) * alpha2'[e])
+ * The workspace's h_scale field is not written.
+ */
+int pmoe_routed_moe_per_tensor(const void* xq, const void* x_sf,
+                               const void* topk_ids, int ids_type, const float* topk_w,
+                               int T, int K, int E, int H, int I, int N1, int expert_offset,
+                               const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                               const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                               const float* a2_scale, int act, void* ws, size_t ws_bytes,
+                               void* out, void* stream);
+
+/*
+ * The routed path with BF16 activations and NVFP4 weights (W4A16, the
+ * 'weight_only' recipe) [Megatron-LM #8262 . How to extend, 'weight_only';
+ * FlashInfer #5019 . Tensor and numerical contract, 'Compute order'].
+ *   x       : BF16 [T, H] activations, not quantized
+ *   weights : output of pmoe_prepare_weights (alphas = 1 / w_scale)
+ * Per valid route, row r:
+ *   y = fp32(sum_k x[t,k] * dec(W1[e,:,k])) * alpha1[e]     (BF16 x BF16 MFMA, FP32 sum)
+ *   h = bf16(max(y,0)^2  or  silu(y_gate) * y_up)           (activation in FP32, one rounding)
+ *   z = bf16(fp32(sum_k h[r,k] * dec(W2[e,:,k])) * alpha2[e])
+ * then the same fixed-order finalize. The workspace's h field holds BF16 h;
+ * hq, h_sf and h_scale are not written. Other arguments as pmoe_routed_moe.
+ */
+int pmoe_routed_moe_w4a16(const void* x, const void* topk_ids, int ids_type, const float* topk_w,
                           int T, int K, int E, int H, int I, int N1, int expert_offset,
                           const void* w1_codes, const void* w1_scales, const float* w1_alpha,
                           const void* w2_codes, const void* w2_scales, const float* w2_alpha,

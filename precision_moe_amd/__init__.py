@@ -38,6 +38,13 @@ _SIGNATURES = {
     "pmoe_routed_moe_steps": (_i, [_i, _i, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
     "pmoe_finalize": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "pmoe_prepare_weights_per_tensor": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pmoe_quantize_input_per_tensor": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp]),
+    "pmoe_routed_moe_per_tensor": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
+    "pmoe_routed_moe_w4a16": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
 }
 STEP_ROUTE, STEP_FC1, STEP_REQUANT, STEP_FC2, STEP_FINALIZE = range(5)
 
@@ -123,8 +130,12 @@ def empty_weights(E, N1, H, I, device):
                            torch.empty(E, **f32))
 
 
-def prepare_weights(w1, w2, out=None, workspace=None, stream=None):
-    """BF16 FC1 [E, N1, H] and FC2 [E, H, I] -> PreparedWeights (in place into `out` if given)."""
+def prepare_weights(w1, w2, out=None, workspace=None, stream=None, input_scales=None):
+    """BF16 FC1 [E, N1, H] and FC2 [E, H, I] -> PreparedWeights (in place into `out` if given).
+
+    input_scales = (a1, a2), device float32 scalars, selects the per-tensor
+    recipe: the static input scales are folded into the alphas.
+    """
     import torch
     E, N1, H = w1.shape
     I = w2.shape[2]
@@ -138,11 +149,25 @@ def prepare_weights(w1, w2, out=None, workspace=None, stream=None):
     need = lib().pmoe_prepare_workspace_bytes(E, N1, H, I)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=w1.device)
-    _check(lib().pmoe_prepare_weights(
-        _ptr(w1), _ptr(w2), E, N1, H, I, _ptr(out.w1_codes), _ptr(out.w1_scales), _ptr(out.w1_alpha),
-        _ptr(out.w2_codes), _ptr(out.w2_scales), _ptr(out.w2_alpha), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+    if input_scales is None:
+        _check(lib().pmoe_prepare_weights(
+            _ptr(w1), _ptr(w2), E, N1, H, I, _ptr(out.w1_codes), _ptr(out.w1_scales),
+            _ptr(out.w1_alpha), _ptr(out.w2_codes), _ptr(out.w2_scales), _ptr(out.w2_alpha),
+            _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        a1, a2 = (_f32_scalar(a) for a in input_scales)
+        _check(lib().pmoe_prepare_weights_per_tensor(
+            _ptr(w1), _ptr(w2), E, N1, H, I, _ptr(a1), _ptr(a2), _ptr(out.w1_codes),
+            _ptr(out.w1_scales), _ptr(out.w1_alpha), _ptr(out.w2_codes), _ptr(out.w2_scales),
+            _ptr(out.w2_alpha), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def _f32_scalar(a):
+    import torch
+    if not (torch.is_tensor(a) and a.dtype == torch.float32 and a.numel() == 1 and a.is_cuda):
+        raise TypeError("static scales are device float32 tensors of one element")
+    return a
 
 
 # ----------------------------------------------------------------------------- quantizers
@@ -159,6 +184,20 @@ def quantize_input_per_token(x, out=None, stream=None):
     _check(lib().pmoe_quantize_input_per_token(_ptr(x), T, H, _ptr(xq), _ptr(xsf), _ptr(xs),
                                                _stream(stream)))
     return xq, xsf, xs
+
+
+def quantize_input_per_tensor(x, a1, out=None, stream=None):
+    """BF16 [T, H] with a static scale a1 (device float32 scalar) -> (xq [T, H/2], x_sf [T, H/16])."""
+    import torch
+    T, H = x.shape
+    x = _bf16_storage(x.contiguous())
+    if out is None:
+        out = (torch.empty((T, H // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((T, H // 16), dtype=torch.uint8, device=x.device))
+    xq, xsf = out
+    _check(lib().pmoe_quantize_input_per_tensor(_ptr(x), T, H, _ptr(_f32_scalar(a1)), _ptr(xq),
+                                                _ptr(xsf), _stream(stream)))
+    return xq, xsf
 
 
 def quantize_rows_f32(h, out=None, stream=None):
@@ -207,6 +246,7 @@ def workspace_views(ws, T, K, E, H, I, act):
         "expert_offsets": view("expert_offsets", E + 1, torch.int32),
         "counters": view("counters", 4, torch.int32),
         "h": view("h", TK * I, torch.float32).view(TK, I),
+        "h_bf16": view("h", TK * I, torch.int16).view(TK, I),    # W4A16: BF16 h in the same field
         "hq": view("hq", TK * I // 2, torch.uint8).view(TK, I // 2),
         "h_sf": view("h_sf", TK * I // 16, torch.uint8).view(TK, I // 16),
         "h_scale": view("h_scale", TK, torch.float32),
@@ -247,6 +287,62 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, ac
         W.E, W.H, W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
         _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, _ptr(workspace),
         workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def _routing_args(topk_ids, topk_w):
+    import torch
+    if topk_ids.dtype == torch.int32:
+        ids_type = IDS_INT32
+    elif topk_ids.dtype == torch.int64:
+        ids_type = IDS_INT64
+    else:
+        raise TypeError("topk_ids must be int32 or int64")
+    if topk_w.dtype != torch.float32:
+        raise TypeError("topk_w must be float32")
+    return topk_ids.contiguous(), ids_type, topk_w.contiguous()
+
+
+def _moe_buffers(T, K, W, act, device, workspace, out):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(moe_workspace_bytes(T, K, W.E, W.H, W.I, act), 256),
+                                dtype=torch.uint8, device=device)
+    if out is None:
+        out = torch.empty((T, W.H), dtype=torch.bfloat16, device=device)
+    return workspace, out
+
+
+def routed_moe_per_tensor(xq, x_sf, topk_ids, topk_w, weights: PreparedWeights, a2, act=None,
+                          expert_offset=0, workspace=None, out=None, stream=None):
+    """Per-tensor NVFP4 recipe: (xq, x_sf) from quantize_input_per_tensor, weights prepared
+    with input_scales=(a1, a2), a2 the static FC2 input scale (device float32 scalar)."""
+    T, K = topk_ids.shape
+    W = weights
+    act = W.act if act is None else act
+    topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
+    workspace, out = _moe_buffers(T, K, W, act, xq.device, workspace, out)
+    _check(lib().pmoe_routed_moe_per_tensor(
+        _ptr(xq), _ptr(x_sf), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1,
+        expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes),
+        _ptr(W.w2_scales), _ptr(W.w2_alpha), _ptr(_f32_scalar(a2)), act, _ptr(workspace),
+        workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def routed_moe_w4a16(x, topk_ids, topk_w, weights: PreparedWeights, act=None, expert_offset=0,
+                     workspace=None, out=None, stream=None):
+    """W4A16 (weight_only) recipe: BF16 activations x [T, H], NVFP4 weights from prepare_weights."""
+    T, K = topk_ids.shape
+    W = weights
+    act = W.act if act is None else act
+    x = _bf16_storage(x.contiguous())
+    topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
+    workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
+    _check(lib().pmoe_routed_moe_w4a16(
+        _ptr(x), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1, expert_offset,
+        _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes), _ptr(W.w2_scales),
+        _ptr(W.w2_alpha), act, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
 

@@ -183,10 +183,12 @@ PMOE_EXPORT size_t pmoe_prepare_workspace_bytes(int E, int N1, int H, int I) {
   return prepare_ws(E, N1, H, I);
 }
 
-PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, int I,
-                                     void* w1_codes, void* w1_scales, float* w1_alpha,
-                                     void* w2_codes, void* w2_scales, float* w2_alpha, void* ws,
-                                     size_t ws_bytes, void* stream) {
+namespace {
+
+int prepare_weights(const void* w1, const void* w2, int E, int N1, int H, int I, const float* a1,
+                    const float* a2, void* w1_codes, void* w1_scales, float* w1_alpha,
+                    void* w2_codes, void* w2_scales, float* w2_alpha, void* ws, size_t ws_bytes,
+                    void* stream) {
   PMOE_TRY(check_weight_shape(E, N1, H, I));
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(w1, 16, "w1"));
@@ -198,6 +200,10 @@ PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int 
   PMOE_TRY(check_ptr(w2_scales, 16, "w2_scales"));
   PMOE_TRY(check_ptr(w2_alpha, 4, "w2_alpha"));
   PMOE_TRY(check_ptr(ws, 16, "ws"));
+  if (a1 || a2) {
+    PMOE_TRY(check_ptr(a1, 4, "a1_scale"));
+    PMOE_TRY(check_ptr(a2, 4, "a2_scale"));
+  }
   const size_t need = prepare_ws(E, N1, H, I);
   if (ws_bytes < need)
     return fail(PMOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
@@ -206,13 +212,34 @@ PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int 
   float* part2 = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                           align_up((size_t)E * weight_amax_parts((long)N1 * H) * 4));
   const int gated_I = (N1 == 2 * I) ? I : 0;
-  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w1), E, N1, H, gated_I, part1,
+  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w1), E, N1, H, gated_I, part1, a1,
                              static_cast<uint8_t*>(w1_codes), static_cast<uint8_t*>(w1_scales),
                              w1_alpha, s));
-  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w2), E, H, I, 0, part2,
+  PMOE_HIP(launch_prepare_fc(static_cast<const uint16_t*>(w2), E, H, I, 0, part2, a2,
                              static_cast<uint8_t*>(w2_codes), static_cast<uint8_t*>(w2_scales),
                              w2_alpha, s));
   return ok();
+}
+
+}  // namespace
+
+PMOE_EXPORT int pmoe_prepare_weights(const void* w1, const void* w2, int E, int N1, int H, int I,
+                                     void* w1_codes, void* w1_scales, float* w1_alpha,
+                                     void* w2_codes, void* w2_scales, float* w2_alpha, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return prepare_weights(w1, w2, E, N1, H, I, nullptr, nullptr, w1_codes, w1_scales, w1_alpha,
+                         w2_codes, w2_scales, w2_alpha, ws, ws_bytes, stream);
+}
+
+PMOE_EXPORT int pmoe_prepare_weights_per_tensor(const void* w1, const void* w2, int E, int N1,
+                                                int H, int I, const float* a1_scale,
+                                                const float* a2_scale, void* w1_codes,
+                                                void* w1_scales, float* w1_alpha, void* w2_codes,
+                                                void* w2_scales, float* w2_alpha, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  if (!a1_scale || !a2_scale) return fail(PMOE_ERR_POINTER, "a1_scale and a2_scale are required");
+  return prepare_weights(w1, w2, E, N1, H, I, a1_scale, a2_scale, w1_codes, w1_scales, w1_alpha,
+                         w2_codes, w2_scales, w2_alpha, ws, ws_bytes, stream);
 }
 
 PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void* xq, void* x_sf,
@@ -225,8 +252,25 @@ PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void*
   PMOE_TRY(check_ptr(xq, 16, "xq"));
   PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
   PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
-  PMOE_HIP(launch_quantize_bf16(x, T, H, static_cast<uint8_t*>(xq), static_cast<uint8_t*>(x_sf),
-                                x_scale, static_cast<hipStream_t>(stream)));
+  PMOE_HIP(launch_quantize_bf16(x, T, H, nullptr, static_cast<uint8_t*>(xq),
+                                static_cast<uint8_t*>(x_sf), x_scale,
+                                static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+PMOE_EXPORT int pmoe_quantize_input_per_tensor(const void* x, int T, int H, const float* a1_scale,
+                                               void* xq, void* x_sf, void* stream) {
+  if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(x, 16, "x"));
+  PMOE_TRY(check_ptr(a1_scale, 4, "a1_scale"));
+  PMOE_TRY(check_ptr(xq, 16, "xq"));
+  PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
+  PMOE_HIP(launch_quantize_bf16(x, T, H, a1_scale, static_cast<uint8_t*>(xq),
+                                static_cast<uint8_t*>(x_sf), nullptr,
+                                static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -240,7 +284,7 @@ PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, v
   PMOE_TRY(check_ptr(hq, 16, "hq"));
   PMOE_TRY(check_ptr(h_sf, 4, "h_sf"));
   PMOE_TRY(check_ptr(h_scale, 4, "h_scale"));
-  PMOE_HIP(launch_quantize_f32(h, R, nullptr, L, static_cast<uint8_t*>(hq),
+  PMOE_HIP(launch_quantize_f32(h, R, nullptr, L, nullptr, static_cast<uint8_t*>(hq),
                                static_cast<uint8_t*>(h_sf), h_scale, static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -259,14 +303,21 @@ PMOE_EXPORT int pmoe_moe_workspace_layout(int T, int K, int E, int H, int I, int
   return ok();
 }
 
-PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const void* x_sf,
-                                      const float* x_scale, const void* topk_ids, int ids_type,
-                                      const float* topk_w, int T, int K, int E, int H, int I, int N1,
-                                      int expert_offset, const void* w1_codes,
-                                      const void* w1_scales, const float* w1_alpha,
-                                      const void* w2_codes, const void* w2_scales,
-                                      const float* w2_alpha, int act, void* ws, size_t ws_bytes,
-                                      void* out, void* stream) {
+namespace {
+
+enum Recipe { kPerToken = 0, kPerTensor = 1, kW4A16 = 2 };
+
+// Steps first..last of the routed path under one recipe.
+//   per-token : x = xq, x_sf, x_scale (per-token NVFP4); requant per row.
+//   per-tensor: x = xq, x_sf (static scale folded into the alphas); x_scale
+//               null; the intermediate is quantized with the static a2.
+//   W4A16     : x = BF16 activations; FC1 writes BF16 h, FC2 reads it.
+int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, const float* x_scale,
+             const float* a2, const void* topk_ids, int ids_type, const float* topk_w, int T, int K,
+             int E, int H, int I, int N1, int expert_offset, const void* w1_codes,
+             const void* w1_scales, const float* w1_alpha, const void* w2_codes,
+             const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
+             void* out, void* stream) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
   PMOE_TRY(check_moe_shape(T, K, E, H, I, act));
@@ -278,9 +329,14 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
     return fail(PMOE_ERR_ARG, "ids_type must be PMOE_IDS_INT32 or PMOE_IDS_INT64");
   if (T == 0) return ok();
   PMOE_TRY(check_device());
-  PMOE_TRY(check_ptr(xq, 16, "xq"));
-  PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
-  PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  if (rc == kW4A16) {
+    PMOE_TRY(check_ptr(x, 16, "x"));
+  } else {
+    PMOE_TRY(check_ptr(x, 16, "xq"));
+    PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
+  }
+  if (rc == kPerToken) PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  if (rc == kPerTensor) PMOE_TRY(check_ptr(a2, 4, "a2_scale"));
   PMOE_TRY(check_ptr(topk_ids, ids_type == PMOE_IDS_INT64 ? 8 : 4, "topk_ids"));
   PMOE_TRY(check_ptr(topk_w, 4, "topk_w"));
   PMOE_TRY(check_ptr(w1_codes, 16, "w1_codes"));
@@ -310,17 +366,19 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
   if (run(PMOE_STEP_ROUTE))
     PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
 
-  float* h = reinterpret_cast<float*>(base + L.off[PMOE_WS_H]);
+  void* h = base + L.off[PMOE_WS_H];  // FP32 h, or BF16 h under W4A16
   uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.off[PMOE_WS_HQ]);
   uint8_t* h_sf = reinterpret_cast<uint8_t*>(base + L.off[PMOE_WS_H_SF]);
   float* h_scale = reinterpret_cast<float*>(base + L.off[PMOE_WS_H_SCALE]);
   uint16_t* z = reinterpret_cast<uint16_t*>(base + L.off[PMOE_WS_Z]);
+  const bool bf16_a = rc == kW4A16;
 
   FcParams p1;
-  p1.a_codes = static_cast<const uint8_t*>(xq);
+  p1.a_codes = static_cast<const uint8_t*>(x);
   p1.a_sf = static_cast<const uint8_t*>(x_sf);
   p1.a_rows = T;
-  p1.a_scale = x_scale;
+  p1.a_bf16 = bf16_a;
+  p1.a_scale = rc == kPerToken ? x_scale : nullptr;
   p1.route_of_row = rb.route_of_row;
   p1.topk = K;
   p1.w_codes = static_cast<const uint8_t*>(w1_codes);
@@ -336,13 +394,15 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
   p1.out_stride = I;
   if (run(PMOE_STEP_FC1)) PMOE_HIP(launch_fc(act == PMOE_ACT_SWIGLU ? kFc1Swiglu : kFc1Relu2, p1, s));
 
-  if (run(PMOE_STEP_REQUANT)) PMOE_HIP(launch_quantize_f32(h, TK, rb.counters, I, hq, h_sf, h_scale, s));
+  if (run(PMOE_STEP_REQUANT) && rc != kW4A16)
+    PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, rb.counters, I,
+                                 rc == kPerTensor ? a2 : nullptr, hq, h_sf, h_scale, s));
 
   FcParams p2 = p1;
-  p2.a_codes = hq;
+  p2.a_codes = bf16_a ? static_cast<const uint8_t*>(h) : hq;
   p2.a_sf = h_sf;
   p2.a_rows = TK;
-  p2.a_scale = h_scale;
+  p2.a_scale = rc == kPerToken ? h_scale : nullptr;
   p2.route_of_row = nullptr;
   p2.w_codes = static_cast<const uint8_t*>(w2_codes);
   p2.w_scales = static_cast<const uint8_t*>(w2_scales);
@@ -358,16 +418,55 @@ PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const
   return ok();
 }
 
+}  // namespace
+
+PMOE_EXPORT int pmoe_routed_moe_steps(int first, int last, const void* xq, const void* x_sf,
+                                      const float* x_scale, const void* topk_ids, int ids_type,
+                                      const float* topk_w, int T, int K, int E, int H, int I, int N1,
+                                      int expert_offset, const void* w1_codes,
+                                      const void* w1_scales, const float* w1_alpha,
+                                      const void* w2_codes, const void* w2_scales,
+                                      const float* w2_alpha, int act, void* ws, size_t ws_bytes,
+                                      void* out, void* stream) {
+  return moe_path(kPerToken, first, last, xq, x_sf, x_scale, nullptr, topk_ids, ids_type, topk_w, T,
+                  K, E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha, w2_codes, w2_scales,
+                  w2_alpha, act, ws, ws_bytes, out, stream);
+}
+
 PMOE_EXPORT int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
                                 const void* topk_ids, int ids_type, const float* topk_w, int T,
                                 int K, int E, int H, int I, int N1, int expert_offset,
                                 const void* w1_codes, const void* w1_scales, const float* w1_alpha,
                                 const void* w2_codes, const void* w2_scales, const float* w2_alpha,
                                 int act, void* ws, size_t ws_bytes, void* out, void* stream) {
-  return pmoe_routed_moe_steps(PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, x_scale, topk_ids,
-                               ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes,
-                               w1_scales, w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes,
-                               out, stream);
+  return moe_path(kPerToken, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, x_scale, nullptr,
+                  topk_ids, ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales,
+                  w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream);
+}
+
+PMOE_EXPORT int pmoe_routed_moe_per_tensor(const void* xq, const void* x_sf, const void* topk_ids,
+                                           int ids_type, const float* topk_w, int T, int K, int E,
+                                           int H, int I, int N1, int expert_offset,
+                                           const void* w1_codes, const void* w1_scales,
+                                           const float* w1_alpha, const void* w2_codes,
+                                           const void* w2_scales, const float* w2_alpha,
+                                           const float* a2_scale, int act, void* ws,
+                                           size_t ws_bytes, void* out, void* stream) {
+  return moe_path(kPerTensor, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, nullptr, a2_scale,
+                  topk_ids, ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales,
+                  w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream);
+}
+
+PMOE_EXPORT int pmoe_routed_moe_w4a16(const void* x, const void* topk_ids, int ids_type,
+                                      const float* topk_w, int T, int K, int E, int H, int I, int N1,
+                                      int expert_offset, const void* w1_codes,
+                                      const void* w1_scales, const float* w1_alpha,
+                                      const void* w2_codes, const void* w2_scales,
+                                      const float* w2_alpha, int act, void* ws, size_t ws_bytes,
+                                      void* out, void* stream) {
+  return moe_path(kW4A16, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, nullptr, nullptr, nullptr,
+                  topk_ids, ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales,
+                  w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream);
 }
 
 PMOE_EXPORT int pmoe_finalize(const void* z, const int32_t* row_of_route, const float* topk_w, int T,

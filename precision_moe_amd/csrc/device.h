@@ -17,6 +17,8 @@ namespace pmoe {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2v_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // fp32(1 / (448 * 6)): the recipe's global constant [Megatron-LM #8262 . What is added].
@@ -116,6 +118,27 @@ __device__ __forceinline__ void decode_scales4(uint32_t s, half2_t& s01, half2_t
 
 // One dword of 8 E2M1 codes (element i in nibble i) times the block scale
 // `sc` -> 8 FP16 values in element order.
+// Eight E2M1 codes (low nibble first) times an FP32 block scale, as BF16. The
+// codes convert exactly to FP32, the product with an E4M3 scale has at most 6
+// significant bits and is exact in FP32, and its low 16 bits are zero, so
+// keeping the high half is the exact BF16 value (gfx950 has no packed BF16
+// multiply).
+__device__ __forceinline__ uint32_t bf16_pair_exact(float2v_t f, float sc) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, f[0] * sc);
+  const uint32_t hi = __builtin_bit_cast(uint32_t, f[1] * sc);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // {hi[31:16], lo[31:16]}
+}
+__device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t w, float sc) {
+  const uint32_t p[4] = {
+      bf16_pair_exact(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), sc),
+      bf16_pair_exact(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), sc),
+      bf16_pair_exact(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), sc),
+      bf16_pair_exact(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), sc)};
+  bf16x8_t r;
+  __builtin_memcpy(&r, p, 16);
+  return r;
+}
+
 __device__ __forceinline__ half8_t decode8(uint32_t w, _Float16 sc) {
   const half2_t s2 = {sc, sc};
   half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;

@@ -38,6 +38,8 @@
 // same weight slab are dispatched together on one XCD and share it through
 // its L2 (a hot expert's weights are fetched once, not once per M-tile), and
 // an expert's activation rows stay in that L2 across its column tiles.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -64,16 +66,42 @@ constexpr int kPrefetch = kRing - 1;               // B chunks in flight ahead o
 
 __host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
 
-__device__ __forceinline__ _Float16 e4m3_to_half(uint32_t b) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false)[0];
+__device__ __forceinline__ floatx16 mfma32(half8_t a, half8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four decoded B fragments (k-steps 0..3 of a 64-chunk) of one column block:
+// FP16 for NVFP4 activations (AK = 0), BF16 for BF16 activations (AK = 1).
+template <int AK>
+struct BFrag {
+  using V = std::conditional_t<AK == 1, bf16x8_t, half8_t>;
+  V b[4];
+  __device__ __forceinline__ BFrag(const uint4& q, uint32_t sc) {
+    half2_t s01, s23;
+    decode_scales4(sc, s01, s23);
+    if constexpr (AK == 1) {
+      b[0] = decode8_bf16(q.x, (float)s01[0]);
+      b[1] = decode8_bf16(q.y, (float)s01[1]);
+      b[2] = decode8_bf16(q.z, (float)s23[0]);
+      b[3] = decode8_bf16(q.w, (float)s23[1]);
+    } else {
+      b[0] = decode8(q.x, s01[0]);
+      b[1] = decode8(q.y, s01[1]);
+      b[2] = decode8(q.z, s23[0]);
+      b[3] = decode8(q.w, s23[1]);
+    }
+  }
+};
 
 // Main loop + epilogue for one tile. TWO: the tile has more than 32 rows, so
 // both row blocks are computed. Every global load inside the loop is
 // unconditional (addresses past the end are clamped to the last chunk and the
 // data is never used), which keeps the in-order load counters exact so the
 // four-chunk B ring really stays in flight.
-template <int MODE, bool TWO>
+template <int MODE, bool TWO, int AK>
 __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
                                         int mrows, int nt) {
@@ -86,35 +114,51 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   // skipped upper block are not filled (t >= 128 when !TWO). Out-of-range
   // buffer reads (the empty half of an odd final stage at the last row)
   // return zeros and are never used.
+  // AK = 0: NVFP4 rows (K/2 bytes of codes + K/16 scales per row), decoded
+  // exactly to FP16 on the way into LDS. AK = 1: BF16 rows (2K bytes), copied
+  // into LDS as they are (W4A16).
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kAQ = AK == 1 ? 4 : 1;             // 16-byte loads per thread and stage
+  const int a_row_bytes = AK == 1 ? KC * 128 : KC * 32;
   const int ar = tid >> 2, aq = tid & 3;
   const bool a_fill = TWO || ar < 32;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)P.a_codes, (short)0, (int)(P.a_rows * KC * 32), kBufFlags);
+      (void*)P.a_codes, (short)0, (int)(P.a_rows * a_row_bytes), kBufFlags);
   const __amdgpu_buffer_rsrc_t a_srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)P.a_sf, (short)0, (int)(P.a_rows * KC * 4), kBufFlags);
-  const uint32_t a_voff = (uint32_t)a_row[ar] * (uint32_t)(KC * 32) + aq * 16;
+      (void*)P.a_sf, (short)0, AK == 1 ? 0 : (int)(P.a_rows * KC * 4), kBufFlags);
+  const uint32_t a_voff = (uint32_t)a_row[ar] * (uint32_t)a_row_bytes + aq * 16 * kAQ;
   const uint32_t a_svoff = (uint32_t)a_row[ar] * (uint32_t)(KC * 4) + aq * 2;
   int a_loff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) a_loff[i] = ar * kLdsRow + (((4 * aq + i) ^ (ar & 15)) << 4);
   struct ARaw {
-    u32x4 q;
+    u32x4 q[kAQ];
     uint32_t s;
   };
   auto a_copy_load = [&](int st, ARaw& v) {
     if (a_fill) {
-      v.q = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff, st * 64, 0);
-      v.s = __builtin_amdgcn_raw_buffer_load_b16(a_srsrc, a_svoff, st * 8, 0);
+      if constexpr (AK == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v.q[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + 16 * i, st * 256, 0);
+      } else {
+        v.q[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff, st * 64, 0);
+        v.s = __builtin_amdgcn_raw_buffer_load_b16(a_srsrc, a_svoff, st * 8, 0);
+      }
     }
   };
   auto a_copy_store = [&](uint8_t* buf, const ARaw& v) {
     if (a_fill) {
-      const half2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.s, 1.0f, false);
-      *reinterpret_cast<half8_t*>(buf + a_loff[0]) = decode8(v.q.x, sc[0]);
-      *reinterpret_cast<half8_t*>(buf + a_loff[1]) = decode8(v.q.y, sc[0]);
-      *reinterpret_cast<half8_t*>(buf + a_loff[2]) = decode8(v.q.z, sc[1]);
-      *reinterpret_cast<half8_t*>(buf + a_loff[3]) = decode8(v.q.w, sc[1]);
+      if constexpr (AK == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(buf + a_loff[i]) = v.q[i];
+      } else {
+        const half2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.s, 1.0f, false);
+        *reinterpret_cast<half8_t*>(buf + a_loff[0]) = decode8(v.q[0].x, sc[0]);
+        *reinterpret_cast<half8_t*>(buf + a_loff[1]) = decode8(v.q[0].y, sc[0]);
+        *reinterpret_cast<half8_t*>(buf + a_loff[2]) = decode8(v.q[0].z, sc[1]);
+        *reinterpret_cast<half8_t*>(buf + a_loff[3]) = decode8(v.q[0].w, sc[1]);
+      }
     }
   };
   // MFMA fragment reads: lane -> row lane%32 (+32 for the upper block), k-chunk
@@ -186,44 +230,31 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     __builtin_amdgcn_sched_barrier(0);
     const uint4 q0 = rq0[i], q1 = rq1[i];
     const uint32_t sc0 = rs0[i], sc1 = rs1[i];
-    half8_t a0[4], a1[4];
+    using AV = typename BFrag<AK>::V;
+    AV a0[4], a1[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a0[j] = *reinterpret_cast<const half8_t*>(abuf + frag[half][j]);
+    for (int j = 0; j < 4; ++j) a0[j] = *reinterpret_cast<const AV*>(abuf + frag[half][j]);
     if constexpr (TWO) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a1[j] = *reinterpret_cast<const half8_t*>(abuf + 32 * kLdsRow + frag[half][j]);
+        a1[j] = *reinterpret_cast<const AV*>(abuf + 32 * kLdsRow + frag[half][j]);
     }
     {
-      half2_t s01, s23;
-      decode_scales4(sc0, s01, s23);
-      const half8_t b0 = decode8(q0.x, s01[0]), b1 = decode8(q0.y, s01[1]);
-      const half8_t b2 = decode8(q0.z, s23[0]), b3 = decode8(q0.w, s23[1]);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[0], b0, acc00, 0, 0, 0);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[1], b1, acc00, 0, 0, 0);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[2], b2, acc00, 0, 0, 0);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[3], b3, acc00, 0, 0, 0);
+      const BFrag<AK> f(q0, sc0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc00 = mfma32(a0[j], f.b[j], acc00);
       if constexpr (TWO) {
-        acc10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[0], b0, acc10, 0, 0, 0);
-        acc10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[1], b1, acc10, 0, 0, 0);
-        acc10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[2], b2, acc10, 0, 0, 0);
-        acc10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[3], b3, acc10, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc10 = mfma32(a1[j], f.b[j], acc10);
       }
     }
     {
-      half2_t s01, s23;
-      decode_scales4(sc1, s01, s23);
-      const half8_t b0 = decode8(q1.x, s01[0]), b1 = decode8(q1.y, s01[1]);
-      const half8_t b2 = decode8(q1.z, s23[0]), b3 = decode8(q1.w, s23[1]);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[0], b0, acc01, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[1], b1, acc01, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[2], b2, acc01, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[3], b3, acc01, 0, 0, 0);
+      const BFrag<AK> f(q1, sc1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc01 = mfma32(a0[j], f.b[j], acc01);
       if constexpr (TWO) {
-        acc11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[0], b0, acc11, 0, 0, 0);
-        acc11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[1], b1, acc11, 0, 0, 0);
-        acc11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[2], b2, acc11, 0, 0, 0);
-        acc11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[3], b3, acc11, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc11 = mfma32(a1[j], f.b[j], acc11);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -274,15 +305,22 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       if (m >= mrows) continue;
       const float s = s_row[m];
       const long orow = (long)(row0 + m) * P.out_stride;
+      // FC1 writes the FP32 activation output (NVFP4 path: it is requantized
+      // next) or its BF16 rounding (W4A16: it is FC2's input as it is).
+      auto store_h = [&](long idx, float h) {
+        if constexpr (AK == 1)
+          static_cast<uint16_t*>(P.out)[idx] = (uint16_t)f32_to_bf16(h);
+        else
+          static_cast<float*>(P.out)[idx] = h;
+      };
       if constexpr (MODE == kFc1Relu2) {
-        float* out = static_cast<float*>(P.out) + orow;
         if (use0) {
           const float y = __builtin_fmaxf(c0[r] * s, 0.0f);
-          out[kColBlock * p0 + n] = y * y;
+          store_h(orow + kColBlock * p0 + n, y * y);
         }
         if (use1) {
           const float y = __builtin_fmaxf(c1[r] * s, 0.0f);
-          out[kColBlock * (p0 + 1) + n] = y * y;
+          store_h(orow + kColBlock * (p0 + 1) + n, y * y);
         }
       } else if constexpr (MODE == kFc1Swiglu) {
         // p0 is even: block p0 holds gate rows, p0 + 1 the matching up rows.
@@ -290,7 +328,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
           const float g = c0[r] * s;
           const float u = c1[r] * s;
           const float silu = g / (1.0f + expf(-g));
-          static_cast<float*>(P.out)[orow + kColBlock * (p0 >> 1) + n] = silu * u;
+          store_h(orow + kColBlock * (p0 >> 1) + n, silu * u);
         }
       } else {
         uint16_t* out = static_cast<uint16_t*>(P.out) + orow;
@@ -301,7 +339,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   }
 }
 
-template <int MODE>
+template <int MODE, int AK>
 __global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
@@ -331,22 +369,31 @@ __global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcPar
     const int r = row0 + min(tid, mrows - 1);  // rows past the tile end repeat a valid row
     const int ar = P.route_of_row ? P.route_of_row[r] / P.topk : r;
     a_row[tid] = ar;
-    s_row[tid] = P.a_scale[ar] * P.w_alpha[e];
+    // per-token / per-row scale times alpha, or the (folded) alpha alone
+    s_row[tid] = P.a_scale ? P.a_scale[ar] * P.w_alpha[e] : P.w_alpha[e];
   }
   __syncthreads();
   if (mrows > 32)
-    fc_tile<MODE, true>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
+    fc_tile<MODE, true, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
   else
-    fc_tile<MODE, false>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
+    fc_tile<MODE, false, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
 }
 
 hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s) {
   const long blocks = (long)p.max_tiles * fc_col_tiles(p.NB);
   const long grid = (blocks + 7) / 8 * 8;
-  switch (mode) {
-    case kFc1Relu2: fc_kernel<kFc1Relu2><<<grid, kThreads, 0, s>>>(p); break;
-    case kFc1Swiglu: fc_kernel<kFc1Swiglu><<<grid, kThreads, 0, s>>>(p); break;
-    case kFc2: fc_kernel<kFc2><<<grid, kThreads, 0, s>>>(p); break;
+  if (p.a_bf16) {
+    switch (mode) {
+      case kFc1Relu2: fc_kernel<kFc1Relu2, 1><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc1Swiglu: fc_kernel<kFc1Swiglu, 1><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc2: fc_kernel<kFc2, 1><<<grid, kThreads, 0, s>>>(p); break;
+    }
+  } else {
+    switch (mode) {
+      case kFc1Relu2: fc_kernel<kFc1Relu2, 0><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc1Swiglu: fc_kernel<kFc1Swiglu, 0><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc2: fc_kernel<kFc2, 0><<<grid, kThreads, 0, s>>>(p); break;
+    }
   }
   return hipGetLastError();
 }

@@ -19,15 +19,20 @@ constexpr int kMaxBlocksPerThread = 4;  // per-row quantizer: rows up to 256*4*1
 constexpr int kMaxRow = 256 * kMaxBlocksPerThread * 16;
 
 // ---------------------------------------------------------------- quantizers
-hipError_t launch_quantize_bf16(const void* x, int T, int H, uint8_t* xq, uint8_t* x_sf,
-                                float* x_scale, hipStream_t s);
-hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, hipStream_t s);
+// static_a: null for per-row scales (written to *_scale), else the device
+// address of a static scale a (rows use g = 1/a; no scale is written).
+hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
+                                uint8_t* x_sf, float* x_scale, hipStream_t s);
+hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L,
+                               const float* static_a, uint8_t* hq, uint8_t* h_sf, float* h_scale,
+                               hipStream_t s);
 
 // ---------------------------------------------------------------- weights
 int weight_amax_parts(long elems);
+// fold_a: null, or the device address of a static input scale folded into alpha.
 hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_I, float* partials,
-                             uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t s);
+                             const float* fold_a, uint8_t* codes, uint8_t* scales, float* alpha,
+                             hipStream_t s);
 
 // ---------------------------------------------------------------- routing
 struct RouteBuffers {
@@ -47,10 +52,11 @@ hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_o
 enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2 };
 
 struct FcParams {
-  const uint8_t* a_codes;    // A rows of Kd/2 bytes (packed E2M1)
-  const uint8_t* a_sf;       // A rows of Kd/16 bytes (E4M3 block scales)
-  long a_rows;               // rows in the A buffers (codes < 4 GiB)
-  const float* a_scale;      // per A row
+  const uint8_t* a_codes;    // A rows of Kd/2 bytes (packed E2M1), or of 2*Kd bytes (BF16)
+  const uint8_t* a_sf;       // A rows of Kd/16 bytes (E4M3 block scales); unused for BF16 A
+  long a_rows;               // rows in the A buffer (< 4 GiB)
+  int a_bf16;                // 1: A is BF16 (W4A16: BF16 MFMA, FC1 writes BF16 h)
+  const float* a_scale;      // per A row, or null (per-tensor / W4A16: alpha alone)
   const int* route_of_row;   // FC1: expert-sorted row -> route (A row = route / topk); FC2: null
   int topk;
   const uint8_t* w_codes;    // prepared layout
@@ -62,7 +68,7 @@ struct FcParams {
   const int* expert_offsets;
   const int* counters;       // [1] = number of M-tiles
   int max_tiles;
-  void* out;                 // FC1: float h [rows][out_stride]; FC2: BF16 z [rows][out_stride]
+  void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z
   int out_stride;
 };
 __host__ __device__ int fc_col_tiles(int NB);

@@ -2,6 +2,10 @@
 // the requantizer of the FP32 expert intermediate (FP32 rows)
 // [Megatron-LM #8262 . Background; What is added; How to extend].
 //
+// With a static scale a (per-tensor recipe [Megatron-LM #8262 . How to
+// extend]) every row uses g = fp32(1 / a) instead of its own amax, read from
+// device memory so that nothing waits on the host; no scale is written.
+//
 // One 256-thread workgroup per row, single pass: thread t owns 16-element
 // blocks t, t+256, ... (at most kMaxBlocksPerThread), keeps them in registers,
 // reduces the row's absolute maximum across the workgroup (max is exact and
@@ -39,10 +43,12 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
 
 // rows: number of rows, or (if rows_dev != nullptr) read from *rows_dev at run
 // time (the intermediate has a device-side count of valid routes).
-template <bool kBf16>
+// static_a: null for per-row scales, else the static scale a (kStatic).
+template <bool kBf16, bool kStatic>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int rows,
                                                             const int* __restrict__ rows_dev,
-                                                            int L, uint8_t* __restrict__ q,
+                                                            int L, const float* __restrict__ static_a,
+                                                            uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             float* __restrict__ scale) {
   __shared__ float red[4];
@@ -60,15 +66,22 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
     const int b = tid + 256 * i;
     if (b < nblk) {
       load_block16<kBf16>(xr, b, v[i]);
+      if constexpr (!kStatic) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][k]));
+        for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][k]));
+      }
     }
   }
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-  const float g = amax * kRecipeConst;
+  float g;
+  if constexpr (kStatic) {
+    g = 1.0f / *static_a;  // IEEE division (correctly rounded)
+  } else {
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    g = amax * kRecipeConst;
+  }
   uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
   uint8_t* sr = sf + row * nblk;
 #pragma unroll
@@ -81,18 +94,27 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
       sr[b] = (uint8_t)s;
     }
   }
-  if (tid == 0) scale[row] = g;
+  if constexpr (!kStatic) {
+    if (tid == 0) scale[row] = g;
+  }
 }
 
-hipError_t launch_quantize_bf16(const void* x, int T, int H, uint8_t* xq, uint8_t* x_sf,
-                                float* x_scale, hipStream_t s) {
-  quantize_rows_kernel<true><<<T, 256, 0, s>>>(x, T, nullptr, H, xq, x_sf, x_scale);
+hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
+                                uint8_t* x_sf, float* x_scale, hipStream_t s) {
+  if (static_a)
+    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, H, static_a, xq, x_sf, nullptr);
+  else
+    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, H, nullptr, xq, x_sf, x_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, hipStream_t s) {
-  quantize_rows_kernel<false><<<R, 256, 0, s>>>(h, R, rows_dev, L, hq, h_sf, h_scale);
+hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L,
+                               const float* static_a, uint8_t* hq, uint8_t* h_sf, float* h_scale,
+                               hipStream_t s) {
+  if (static_a)
+    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, rows_dev, L, static_a, hq, h_sf, nullptr);
+  else
+    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, rows_dev, L, nullptr, hq, h_sf, h_scale);
   return hipGetLastError();
 }
 

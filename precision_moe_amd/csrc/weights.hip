@@ -11,6 +11,9 @@
 //        w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale)
 //      and quantizes every 16-block of its rows with g = alpha, writing codes
 //      and E4M3 scales straight into the prepared layout (see include/pmoe.h).
+//      For the per-tensor recipe the stored alpha folds in the static input
+//      scale a: alpha' = fp32(1 / fp32(w_scale * a)); codes and block scales do
+//      not change [Megatron-LM #8262 . How to extend].
 // Writing into caller buffers in place keeps their addresses fixed across a
 // refresh (in-place refit).
 #include "device.h"
@@ -52,8 +55,8 @@ __global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __rest
 // selects the gate/up interleave of a gated FC1.
 __global__ __launch_bounds__(256) void weight_quant_kernel(
     const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int NBp, int KC,
-    const float* __restrict__ partials, int parts, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ alpha_out) {
+    const float* __restrict__ partials, int parts, const float* __restrict__ fold_a,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ alpha_out) {
   const int p = blockIdx.x, e = blockIdx.y;
   __shared__ float red[4];
   float m = 0.0f;
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
   const float w_scale = 2688.0f / amax;  // +inf for an all-zero expert
   const float alpha = 1.0f / w_scale;    // then 0
-  if (p == 0 && threadIdx.x == 0) alpha_out[e] = alpha;
+  if (p == 0 && threadIdx.x == 0) alpha_out[e] = fold_a ? 1.0f / (w_scale * *fold_a) : alpha;
 
   const int nkb = Kd / kBlock;
   // chunk c of column block p sits at slab ((e*NT + p/8)*KC + c)*8 + p%8
@@ -100,7 +103,8 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
 }
 
 hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_I, float* partials,
-                             uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t s) {
+                             const float* fold_a, uint8_t* codes, uint8_t* scales, float* alpha,
+                             hipStream_t s) {
   const long per_expert = (long)N * Kd;
   const int parts = weight_amax_parts(per_expert);
   weight_amax_kernel<<<dim3(parts, E), 256, 0, s>>>(w, per_expert, parts, partials);
@@ -109,7 +113,7 @@ hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_
   const int NB = N / kColBlock, KC = Kd / kChunk;
   const int NBp = padded_col_blocks(NB);
   weight_quant_kernel<<<dim3(NBp, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, NBp, KC, partials, parts,
-                                                   codes, scales, alpha);
+                                                   fold_a, codes, scales, alpha);
   return hipGetLastError();
 }
 
