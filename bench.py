@@ -143,8 +143,6 @@ def main():
     prepare = {"ms": prep_ms, "GB/s": elems * (2 + NVFP4_BYTES) / (prep_ms * 1e-3) / 1e9,
                "note": "reads BF16 once (algorithmic; the kernel reads it twice) and writes NVFP4"}
     log(f"[bench] prepare_weights {prep_ms:.2f} ms")
-    del w1, w2
-    torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- inputs
     x = synth.activations(w, device=dev).view(torch.bfloat16)
@@ -207,6 +205,44 @@ def main():
     stage_ms = acc / args.stage_reps
 
     views = pm.workspace_views(ws, T, w.K, w.E, w.H, w.I, P.act)
+
+    # ---------------------------------------------------------------- other recipes
+    # The per-tensor NVFP4 and W4A16 variants of the same layer, on the same
+    # inputs: static scales calibrated as 2688 / amax of the FC1 input and of
+    # the per-token run's intermediate (setup, outside the timed region).
+    R_rows = int(views["counters"][0].item())
+    a1 = (2688.0 / x.float().abs().max()).reshape(1).float()
+    a2 = (2688.0 / views["h"][:R_rows].abs().max()).reshape(1).float()
+    P_pt = pm.prepare_weights(w1, w2, input_scales=(a1, a2))
+    del w1, w2
+    torch.cuda.empty_cache()
+    xq_pt = torch.empty_like(xq)
+    xs_pt = torch.empty_like(xs)
+
+    def step_per_tensor():
+        pm.quantize_input_per_tensor(x, a1, out=(xq_pt, xs_pt))
+        pm.routed_moe_per_tensor(xq_pt, xs_pt, ids, wts, P_pt, a2, workspace=ws, out=out)
+
+    def step_w4a16():
+        pm.routed_moe_w4a16(x, ids, wts, P, workspace=ws, out=out)
+
+    recipes = {}
+    flops_step = 2.0 * R_rows * (w.N1 * w.H + w.H * w.I)
+    for name, fn in (("per_tensor", step_per_tensor), ("weight_only_w4a16", step_w4a16)):
+        for _ in range(max(args.warmup // 2, 2)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        recipes[name] = {"ms_per_step": ms, "tokens/s": T / (ms * 1e-3),
+                         "TFLOP/s": flops_step / (ms * 1e-3) / 1e12}
+        log(f"[bench] {name}: {ms * 1e3:.1f} us/step")
+    del P_pt
     counts = np.diff(views["expert_offsets"].cpu().numpy())
     R = int(counts.sum())
     ab = algorithmic_bytes(w, counts, T, R)
@@ -245,6 +281,7 @@ def main():
                      "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3},
         "kernels": kernels,
         "prepare": prepare,
+        "recipes": recipes,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
