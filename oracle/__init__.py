@@ -23,7 +23,10 @@ Modules:
              whole pipeline, and two brute-force references used as pins.
   recipes -- the per-tensor NVFP4 (static calibrated input scales folded into
              the alphas) and weight-only W4A16 (BF16 activations) variants of
-             the pipeline [Megatron-LM #8262 . How to extend].
+             the pipeline [Megatron-LM #8262 . How to extend], and the general
+             pipeline with the layer options (SwiGLU clamp, fused finalize).
+  layer   -- the router front (top-k, softmax weights), the SwiGLU clamp and
+             the fused (order-free) finalize.
 
 Parity pins: every function here is pinned by a CPU test against something
 other than itself (hand enumerations, a library cast, brute force, closed

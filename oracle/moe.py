@@ -267,15 +267,19 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights, act, expert_offset=
 
 
 # ----------------------------------------------------------------------------- references
-def _act64(y, act, inter):
+def _act64(y, act, inter, swiglu_limit=0.0):
     if act == "relu2":
         r = np.maximum(y, 0.0)
         return r * r
     gate, up = y[..., :inter], y[..., inter:]
+    if swiglu_limit:
+        gate = np.minimum(gate, swiglu_limit)
+        up = np.clip(up, -swiglu_limit, swiglu_limit)
     return gate / (1.0 + np.exp(-gate)) * up
 
 
-def brute_force_moe(x_f32, topk_ids, topk_w, w1, w2, act, expert_offset=0, quantize=None):
+def brute_force_moe(x_f32, topk_ids, topk_w, w1, w2, act, expert_offset=0, quantize=None,
+                    swiglu_limit=0.0):
     """Per-token, per-slot float64 MoE with no sorting or grouping.
 
     x_f32 [T, H]; w1 [E, N1, H], w2 [E, H, I] as float arrays. With
@@ -283,7 +287,8 @@ def brute_force_moe(x_f32, topk_ids, topk_w, w1, w2, act, expert_offset=0, quant
         out[t] = sum_j w[t,j] * FC2_e( act( FC1_e(x[t]) ) ),  e = id[t,j] - offset.
     With `quantize` = (qx, qw1, qw2, qh), callables returning dequantized float64
     arrays, the same loop runs on dequantized tensors, requantizing the FP32
-    intermediate with qh.
+    intermediate with qh. swiglu_limit > 0 clamps the SwiGLU inputs (gate from
+    above, up on both sides).
     """
     x = np.asarray(x_f32, np.float64)
     T, K = np.asarray(topk_ids).shape
@@ -301,7 +306,7 @@ def brute_force_moe(x_f32, topk_ids, topk_w, w1, w2, act, expert_offset=0, quant
             if not (0 <= e < E):
                 continue
             y = w1[e] @ x[t]
-            h = _act64(y, act, I)
+            h = _act64(y, act, I, swiglu_limit)
             if quantize is not None:
                 h = qh(h[None].astype(np.float32))[0]
             out[t] += float(topk_w[t][j]) * (w2[e] @ h)

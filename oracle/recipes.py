@@ -31,8 +31,10 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import bf16_to_f32, f32_to_bf16_rne, pack_nibbles
+from .layer import finalize_fused, swiglu_clamp
 from .moe import Routing, Weights, activation, detect_gating, finalize, route, ACTS
-from .quant import block_quantize, dequantize_blocks, quantize_weights, weight_global_scale
+from .quant import (block_quantize, dequantize_blocks, quantize_rows_f32, quantize_weights,
+                    weight_global_scale)
 
 F32 = np.float32
 RECIPES = ("per_token", "per_tensor", "weight_only")
@@ -117,33 +119,51 @@ class RecipeResult:
     out: np.ndarray            # uint16 BF16 [T, H]
     routing: Routing
     h: np.ndarray              # float32 [R, I] FP32 activation output
-    hq: np.ndarray             # per_tensor: uint8 [R, I/2]; weight_only: empty
-    h_sf: np.ndarray           # per_tensor: uint8 [R, I/16]; weight_only: empty
-    h_bf16: np.ndarray         # weight_only: uint16 [R, I] FC2 input; per_tensor: empty
+    hq: np.ndarray             # NVFP4 recipes: uint8 [R, I/2]; weight_only: empty
+    h_sf: np.ndarray           # NVFP4 recipes: uint8 [R, I/16]; weight_only: empty
+    h_bf16: np.ndarray         # weight_only: uint16 [R, I] FC2 input; else empty
     z: np.ndarray              # uint16 BF16 [R, H]
     computed_rows: np.ndarray  # bool [R]
+    zf: np.ndarray = None      # float32 [R, H] unrounded FC2 rows (input of the fused finalize)
 
 
-def _fc_exact(A, wq_e, w_sf_e, alpha_e):
-    """fp32( fp32(A @ w_hat^T) * alpha ) with A float64 holding exact input values."""
+def _fc_exact(A, wq_e, w_sf_e, alpha_e, row_scale=None):
+    """fp32( fp32(A @ w_hat^T) * s ) with A float64 holding exact input values;
+    s = fp32(row_scale * alpha) per row, or alpha alone."""
     B = dequantize_blocks(wq_e, w_sf_e)
     acc = (A @ B.T).astype(F32)
-    return (acc * F32(alpha_e)).astype(F32)
+    if row_scale is None:
+        return (acc * F32(alpha_e)).astype(F32)
+    s = (np.asarray(row_scale, F32) * F32(alpha_e)).astype(F32)
+    return (acc * s[:, None]).astype(F32)
+
+
+def _act(y, act, inter, limit):
+    if act == "swiglu" and limit:
+        gate, up = swiglu_clamp(y[:, :inter], y[:, inter:], limit)
+        y = np.concatenate([gate, up], axis=1)
+    return activation(y, act, inter)
 
 
 def routed_moe_recipe(recipe, x, topk_ids, topk_w, weights, act, expert_offset=0, a2=None,
-                      tokens=None, experts=None):
-    """S2..S6 under the per_tensor or weight_only recipe.
+                      tokens=None, experts=None, swiglu_limit=0.0, finalize_mode="ordered"):
+    """S2..S6 under one recipe, with the layer options.
 
+    per_token  : x = (xq, x_sf, x_scale) from quant.quantize_input_per_token;
+                 the same arithmetic as moe.routed_moe.
     per_tensor : x = (xq, x_sf) from quantize_input_per_tensor; `weights` from
                  prepare_weights_per_tensor (folded alphas); a2 = the static FC2
                  input scale.
     weight_only: x = BF16 activations [T, H] (uint16 bits); `weights` from the
                  per-token preparation (alphas = 1/w_scale).
+    swiglu_limit : SwiGLU clamp limit (reading R25); 0 = none.
+    finalize_mode: "ordered" (fixed slot order, BF16 z) or "fused" (reading R23).
     `tokens` / `experts` restrict the work as in moe.routed_moe.
     """
-    if recipe not in ("per_tensor", "weight_only"):
+    if recipe not in RECIPES:
         raise ValueError(recipe)
+    if finalize_mode not in ("ordered", "fused"):
+        raise ValueError(finalize_mode)
     E, N1, H, I = weights.shape
     gated = detect_gating(N1, I)
     if act not in ACTS or gated != (act == "swiglu"):
@@ -159,7 +179,10 @@ def routed_moe_recipe(recipe, x, topk_ids, topk_w, weights, act, expert_offset=0
         exp_of_row = np.repeat(np.arange(E), rt.counts)
         row_on &= np.isin(exp_of_row, np.asarray(experts))
 
-    if recipe == "per_tensor":
+    x_scale = None
+    if recipe == "per_token":
+        xq, x_sf, x_scale = x
+    elif recipe == "per_tensor":
         xq, x_sf = x
     else:
         x_f64 = bf16_to_f32(x).astype(np.float64)
@@ -175,37 +198,47 @@ def routed_moe_recipe(recipe, x, topk_ids, topk_w, weights, act, expert_offset=0
             continue
         w1q, w1sf, al1, _, _, _ = weights.expert(e)
         t = tok_of_row[rows]
-        A = dequantize_blocks(xq[t], x_sf[t]) if recipe == "per_tensor" else x_f64[t]
-        h[rows] = activation(_fc_exact(A, w1q, w1sf, al1), act, I)
+        A = x_f64[t] if recipe == "weight_only" else dequantize_blocks(xq[t], x_sf[t])
+        rs = x_scale[t] if recipe == "per_token" else None
+        h[rows] = _act(_fc_exact(A, w1q, w1sf, al1, rs), act, I, swiglu_limit)
 
-    hq = np.zeros((R, I // 2) if recipe == "per_tensor" else (0, 0), np.uint8)
-    h_sf = np.zeros((R, I // 16) if recipe == "per_tensor" else (0, 0), np.uint8)
-    h_bf16 = np.zeros((R, I) if recipe == "weight_only" else (0, 0), np.uint16)
+    nvfp4 = recipe != "weight_only"
+    hq = np.zeros((R, I // 2) if nvfp4 else (0, 0), np.uint8)
+    h_sf = np.zeros((R, I // 16) if nvfp4 else (0, 0), np.uint8)
+    h_scale = np.zeros((R,), F32)
+    h_bf16 = np.zeros((R, I) if not nvfp4 else (0, 0), np.uint16)
     if row_on.any():
-        if recipe == "per_tensor":
+        if recipe == "per_token":
+            hq[row_on], h_sf[row_on], h_scale[row_on] = quantize_rows_f32(h[row_on])
+        elif recipe == "per_tensor":
             hq[row_on], h_sf[row_on] = quantize_rows_static(h[row_on], a2)
         else:
             h_bf16[row_on] = f32_to_bf16_rne(h[row_on])
 
     z = np.zeros((R, H), np.uint16)
+    zf = np.zeros((R, H), F32)
     for e in range(E):
         rows = rows_of(e)
         if rows.size == 0:
             continue
         _, _, _, w2q, w2sf, al2 = weights.expert(e)
-        if recipe == "per_tensor":
+        if nvfp4:
             A = dequantize_blocks(hq[rows], h_sf[rows])
         else:
             A = bf16_to_f32(h_bf16[rows]).astype(np.float64)
-        z[rows] = f32_to_bf16_rne(_fc_exact(A, w2q, w2sf, al2))
+        zf[rows] = _fc_exact(A, w2q, w2sf, al2, h_scale[rows] if recipe == "per_token" else None)
+        z[rows] = f32_to_bf16_rne(zf[rows])
 
     if R and experts is None:
-        out = finalize(z, rt.row_of_route, topk_w, T, K)
+        if finalize_mode == "ordered":
+            out = finalize(z, rt.row_of_route, topk_w, T, K)
+        else:
+            out = finalize_fused(zf, rt.row_of_route, topk_w, T, K)
     else:
         out = np.zeros((T, H), np.uint16)
     if tokens is not None:
         out[~want] = 0
-    return RecipeResult(out, rt, h, hq, h_sf, h_bf16, z, row_on)
+    return RecipeResult(out, rt, h, hq, h_sf, h_bf16, z, row_on, zf)
 
 
 # ----------------------------------------------------------------------------- brute force

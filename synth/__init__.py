@@ -250,8 +250,8 @@ def activations(w: Workload, T: int = None, device=None):
     return _as_bf16(x, device)
 
 
-def router(w: Workload, T: int = None):
-    """(topk_ids int32 [T, K], topk_w float32 [T, K]) from softmax over seeded logits (numpy)."""
+def router_logits(w: Workload, T: int = None):
+    """Seeded FP32 router logits [T, E] (the hot experts get +hot_bias)."""
     T = w.T if T is None else T
     g = np.random.Generator(np.random.PCG64([BASE_SEED, w.index, T_LOGITS]))
     if w.logits == "uniform":
@@ -260,6 +260,12 @@ def router(w: Workload, T: int = None):
         logits = g.standard_normal((T, w.E))
     for e in w.hot_experts:
         logits[:, e] += w.hot_bias
+    return logits.astype(np.float32)
+
+
+def router(w: Workload, T: int = None):
+    """(topk_ids int32 [T, K], topk_w float32 [T, K]) from softmax over router_logits (numpy)."""
+    logits = router_logits(w, T).astype(np.float64)
     p = np.exp(logits - logits.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     ids = np.argsort(-p, axis=1, kind="stable")[:, : w.K]

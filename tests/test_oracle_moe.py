@@ -185,18 +185,25 @@ def test_brute_force_is_textbook_moe():
         w2 = rng.standard_normal((E, H, I)) * 0.1
         ids = np.array([[0, 2], [1, 1], [2, 0], [1, 0], [0, -1]])
         wts = rng.random((T, K))
-        got = brute_force_moe(x, ids, wts, w1, w2, act)
-        want = np.zeros((T, H))
-        for j in range(K):
-            e = np.clip(ids[:, j], 0, E - 1)
-            y = np.einsum("tnh,th->tn", w1[e], x)
-            if act == "relu2":
-                h = np.maximum(y, 0) ** 2
-            else:
-                h = y[:, :I] * (1 / (1 + np.exp(-y[:, :I]))) * y[:, I:]
-            z = np.einsum("thi,ti->th", w2[e], h)
-            want += np.where(ids[:, j:j + 1] >= 0, wts[:, j:j + 1] * z, 0)
-        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        for limit in ((0.0, 0.3) if act == "swiglu" else (0.0,)):
+            got = brute_force_moe(x, ids, wts, w1, w2, act, swiglu_limit=limit)
+            want = np.zeros((T, H))
+            for j in range(K):
+                e = np.clip(ids[:, j], 0, E - 1)
+                y = np.einsum("tnh,th->tn", w1[e], x)
+                if act == "relu2":
+                    h = np.maximum(y, 0) ** 2
+                else:
+                    g, u = y[:, :I], y[:, I:]
+                    if limit:
+                        g, u = np.where(g > limit, limit, g), np.where(u > limit, limit,
+                                                                        np.where(u < -limit, -limit, u))
+                    h = g * (1 / (1 + np.exp(-g))) * u
+                z = np.einsum("thi,ti->th", w2[e], h)
+                want += np.where(ids[:, j:j + 1] >= 0, wts[:, j:j + 1] * z, 0)
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+            if limit:
+                assert not np.allclose(got, brute_force_moe(x, ids, wts, w1, w2, act))  # clamp bites
 
 
 def test_expert_offset_and_invalid_routes():

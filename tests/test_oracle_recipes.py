@@ -273,6 +273,6 @@ def test_recipes_batch_invariance_and_plausibility():
 def test_recipe_rejects_unknown_and_mismatch():
     x, w1, w2, ids, wts = _case(2, 32, 16, 2, 1, "relu2", seed=1)
     with pytest.raises(ValueError):
-        routed_moe_recipe("per_token", x, ids, wts, prepare_weights(w1, w2), "relu2")
+        routed_moe_recipe("mxfp8", x, ids, wts, prepare_weights(w1, w2), "relu2")
     with pytest.raises(ValueError):
         routed_moe_recipe("weight_only", x, ids, wts, prepare_weights(w1, w2), "swiglu")
