@@ -309,6 +309,62 @@ int pmoe_routed_moe_w4a16(const void* x, const void* topk_ids, int ids_type, con
                           const void* w2_codes, const void* w2_scales, const float* w2_alpha,
                           int act, void* ws, size_t ws_bytes, void* out, void* stream);
 
+/* Options of pmoe_routed_moe_ex. */
+#define PMOE_RECIPE_PER_TOKEN 0  /* per-token NVFP4 x NVFP4 (x = xq, x_sf, x_scale)        */
+#define PMOE_RECIPE_PER_TENSOR 1 /* per-tensor NVFP4 x NVFP4 (x = xq, x_sf; a2_scale)       */
+#define PMOE_RECIPE_W4A16 2      /* BF16 x NVFP4 (x = BF16 activations)                     */
+#define PMOE_FINALIZE_ORDERED 0  /* fixed slot order, BF16 z per route: batch invariant     */
+#define PMOE_FINALIZE_FUSED 1    /* FP32 atomic adds inside FC2: order-free, not invariant  */
+
+typedef struct pmoe_moe_options {
+  int recipe;             /* PMOE_RECIPE_*                                                  */
+  int finalize;           /* PMOE_FINALIZE_*                                                */
+  float swiglu_limit;     /* > 0: SwiGLU clamp, gate <= L and -L <= up <= L; 0: none         */
+  const float* a2_scale;  /* per-tensor recipe: device float32 scalar; otherwise NULL       */
+} pmoe_moe_options;
+
+/*
+ * The routed path with options; options == NULL means per-token, ordered, no
+ * clamp (exactly pmoe_routed_moe).
+ *   recipe       : which entry point's contract x / x_sf / x_scale and the
+ *                  weights follow (pmoe_routed_moe, pmoe_routed_moe_per_tensor,
+ *                  pmoe_routed_moe_w4a16; unused inputs may be NULL).
+ *   finalize     : PMOE_FINALIZE_FUSED is the order-free mode the two-stage
+ *                  finalize replaces [Megatron-LM #8262 . What is added; Why
+ *                  CuTe DSL, 'Controllable determinism']: each route's FC2
+ *                  value fp32(acc * scale), times its routing weight, is added
+ *                  with FP32 atomics into a per-token FP32 row that is rounded
+ *                  to BF16 once. The order of additions is not fixed, so the
+ *                  result may differ in the last FP32 bits between runs and is
+ *                  not batch invariant; z is not written.
+ *   swiglu_limit : the clamp of [FlashInfer #5019 . Tensor and numerical
+ *                  contract, 'Compute order']; PMOE_ERR_ARG unless act is
+ *                  SwiGLU (or the limit is 0).
+ * Other arguments, layout and errors as the recipe's own entry point.
+ */
+int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float* x_scale,
+                       const void* topk_ids, int ids_type, const float* topk_w,
+                       int T, int K, int E, int H, int I, int N1, int expert_offset,
+                       const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                       const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                       int act, const pmoe_moe_options* options,
+                       void* ws, size_t ws_bytes, void* out, void* stream);
+
+/*
+ * Router front: top-k experts and their routing weights from FP32 logits
+ * (plain top-k, no group-limited routing [Megatron-LM #8262 . Performance]).
+ *   logits    : float32 [T, E], finite, 1 <= E <= 1024
+ *   topk_ids  : int32 [T, K] out, 1 <= K <= min(32, E): the K largest logits,
+ *               larger first, equal logits ordered by lower expert id (exact:
+ *               the choice is made on the logits, and softmax preserves order)
+ *   topk_w    : float32 [T, K] out: p = exp(l - max) / sum_e exp(l_e - max) in
+ *               FP32 (deterministic order), divided by the sum of the K chosen
+ *               p (in slot order) when renormalize == 1
+ * Alignment: 4 bytes.
+ */
+int pmoe_router_topk(const float* logits, int T, int E, int K, int renormalize,
+                     int32_t* topk_ids, float* topk_w, void* stream);
+
 /*
  * Deterministic two-stage finalize, standalone [Megatron-LM #8262 . Background,
  * 'two-stage finalize'; FlashInfer #5019 . Tensor and numerical contract]:

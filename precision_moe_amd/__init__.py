@@ -16,12 +16,22 @@ LIB_PATH = os.environ.get("PMOE_LIB") or os.path.join(_HERE, "_lib", "libpmoe.so
 
 ACT_RELU2, ACT_SWIGLU = 0, 1
 IDS_INT32, IDS_INT64 = 0, 1
+RECIPE_PER_TOKEN, RECIPE_PER_TENSOR, RECIPE_W4A16 = 0, 1, 2
+FINALIZE_ORDERED, FINALIZE_FUSED = 0, 1
+_RECIPES = {"per_token": RECIPE_PER_TOKEN, "per_tensor": RECIPE_PER_TENSOR, "w4a16": RECIPE_W4A16}
+_FINALIZE = {"ordered": FINALIZE_ORDERED, "fused": FINALIZE_FUSED}
 WS_FIELDS = ("row_of_route", "route_of_row", "expert_offsets", "counters", "h", "hq", "h_sf",
              "h_scale", "z")
 
 _c_size_p = ctypes.POINTER(ctypes.c_size_t)
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
+
+
+class MoeOptions(ctypes.Structure):
+    """pmoe_moe_options (include/pmoe.h)."""
+    _fields_ = [("recipe", ctypes.c_int), ("finalize", ctypes.c_int),
+                ("swiglu_limit", ctypes.c_float), ("a2_scale", ctypes.c_void_p)]
 _SIGNATURES = {
     "pmoe_version": (_i, []),
     "pmoe_last_error": (ctypes.c_char_p, []),
@@ -45,6 +55,10 @@ _SIGNATURES = {
                                         _vp, _vp, _vp, _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
     "pmoe_routed_moe_w4a16": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
+    "pmoe_routed_moe_ex": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _i, ctypes.POINTER(MoeOptions), _vp,
+                                ctypes.c_size_t, _vp, _vp]),
+    "pmoe_router_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp]),
 }
 STEP_ROUTE, STEP_FC1, STEP_REQUANT, STEP_FC2, STEP_FINALIZE = range(5)
 
@@ -344,6 +358,45 @@ def routed_moe_w4a16(x, topk_ids, topk_w, weights: PreparedWeights, act=None, ex
         _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes), _ptr(W.w2_scales),
         _ptr(W.w2_alpha), act, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, recipe="per_token",
+                  finalize="ordered", swiglu_limit=0.0, a2=None, act=None, expert_offset=0,
+                  workspace=None, out=None, stream=None):
+    """The routed path with options (pmoe_routed_moe_ex): recipe "per_token" (x = xq, x_sf,
+    x_scale), "per_tensor" (x = xq, x_sf; a2) or "w4a16" (x = BF16 activations; x_sf, x_scale
+    None); finalize "ordered" or "fused"; swiglu_limit > 0 clamps SwiGLU."""
+    T, K = topk_ids.shape
+    W = weights
+    act = W.act if act is None else act
+    topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
+    if recipe == "w4a16":
+        x = _bf16_storage(x.contiguous())
+    workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
+    opt = MoeOptions(_RECIPES[recipe], _FINALIZE[finalize], float(swiglu_limit),
+                     _f32_scalar(a2).data_ptr() if a2 is not None else None)
+    _check(lib().pmoe_routed_moe_ex(
+        _ptr(x), _ptr(x_sf), _ptr(x_scale), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H,
+        W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
+        _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, ctypes.byref(opt),
+        _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def router_topk(logits, k, renormalize=False, out=None, stream=None):
+    """FP32 logits [T, E] -> (topk_ids int32 [T, k], topk_w float32 [T, k])."""
+    import torch
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    logits = logits.contiguous()
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=logits.device),
+               torch.empty((T, k), dtype=torch.float32, device=logits.device))
+    ids, w = out
+    _check(lib().pmoe_router_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
+                                  _stream(stream)))
+    return ids, w
 
 
 def finalize(z, row_of_route, topk_w, out=None, stream=None):

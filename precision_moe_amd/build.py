@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libpmoe.so")
-SOURCES = ["api.hip", "quantize.hip", "weights.hip", "route.hip", "gemm.hip", "finalize.hip"]
+SOURCES = ["api.hip", "quantize.hip", "weights.hip", "route.hip", "gemm.hip", "finalize.hip",
+           "router.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

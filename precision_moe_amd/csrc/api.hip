@@ -115,7 +115,7 @@ size_t prepare_ws(int E, int N1, int H, int I) {
 // routed_moe workspace layout
 struct MoeLayout {
   size_t off[PMOE_WS_NUM_FIELDS];
-  size_t rank_local, block_counts, tiles;
+  size_t rank_local, block_counts, tiles, acc32;
   size_t total;
   int max_tiles;
 };
@@ -142,6 +142,7 @@ MoeLayout moe_layout(int T, int K, int E, int H, int I) {
   L.rank_local = take(TK * 4);
   L.block_counts = take((size_t)route_blocks((int)TK) * E * 4);
   L.tiles = take((size_t)L.max_tiles * 4 * 4);
+  L.acc32 = take((size_t)T * H * 4);
   L.total = o;
   return L;
 }
@@ -305,21 +306,25 @@ PMOE_EXPORT int pmoe_moe_workspace_layout(int T, int K, int E, int H, int I, int
 
 namespace {
 
-enum Recipe { kPerToken = 0, kPerTensor = 1, kW4A16 = 2 };
+enum Recipe { kPerToken = PMOE_RECIPE_PER_TOKEN, kPerTensor = PMOE_RECIPE_PER_TENSOR,
+              kW4A16 = PMOE_RECIPE_W4A16 };
 
 // Steps first..last of the routed path under one recipe.
 //   per-token : x = xq, x_sf, x_scale (per-token NVFP4); requant per row.
 //   per-tensor: x = xq, x_sf (static scale folded into the alphas); x_scale
 //               null; the intermediate is quantized with the static a2.
 //   W4A16     : x = BF16 activations; FC1 writes BF16 h, FC2 reads it.
+// fused: the order-free finalize inside FC2 (FP32 atomics) instead of the
+// fixed-order one; swiglu_limit > 0 clamps the SwiGLU inputs.
 int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, const float* x_scale,
              const float* a2, const void* topk_ids, int ids_type, const float* topk_w, int T, int K,
              int E, int H, int I, int N1, int expert_offset, const void* w1_codes,
              const void* w1_scales, const float* w1_alpha, const void* w2_codes,
              const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
-             void* out, void* stream) {
+             void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
+  if (!(swiglu_limit >= 0.0f)) return fail(PMOE_ERR_ARG, "swiglu_limit must be >= 0");
   PMOE_TRY(check_moe_shape(T, K, E, H, I, act));
   if (N1 != I && N1 != 2 * I) return fail(PMOE_ERR_SHAPE, "FC1 width N1 must be I or 2*I");
   if ((N1 == 2 * I) != (act == PMOE_ACT_SWIGLU))
@@ -392,6 +397,9 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p1.max_tiles = L.max_tiles;
   p1.out = h;
   p1.out_stride = I;
+  p1.swiglu_limit = swiglu_limit;
+  p1.out_route = nullptr;
+  p1.out_w = nullptr;
   if (run(PMOE_STEP_FC1)) PMOE_HIP(launch_fc(act == PMOE_ACT_SWIGLU ? kFc1Swiglu : kFc1Relu2, p1, s));
 
   if (run(PMOE_STEP_REQUANT) && rc != kW4A16)
@@ -411,10 +419,23 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p2.KC = I / kChunk;
   p2.out = z;
   p2.out_stride = H;
-  if (run(PMOE_STEP_FC2)) PMOE_HIP(launch_fc(kFc2, p2, s));
+  float* acc32 = reinterpret_cast<float*>(base + L.acc32);
+  if (fused) {
+    p2.out = acc32;
+    p2.out_route = rb.route_of_row;
+    p2.out_w = topk_w;
+  }
+  if (run(PMOE_STEP_FC2)) {
+    if (fused) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+    PMOE_HIP(launch_fc(fused ? kFc2Fused : kFc2, p2, s));
+  }
 
-  if (run(PMOE_STEP_FINALIZE))
-    PMOE_HIP(launch_finalize(z, rb.row_of_route, topk_w, T, K, H, static_cast<uint16_t*>(out), s));
+  if (run(PMOE_STEP_FINALIZE)) {
+    if (fused)
+      PMOE_HIP(launch_f32_to_bf16(acc32, (long)T * H, static_cast<uint16_t*>(out), s));
+    else
+      PMOE_HIP(launch_finalize(z, rb.row_of_route, topk_w, T, K, H, static_cast<uint16_t*>(out), s));
+  }
   return ok();
 }
 
@@ -455,6 +476,49 @@ PMOE_EXPORT int pmoe_routed_moe_per_tensor(const void* xq, const void* x_sf, con
   return moe_path(kPerTensor, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, nullptr, a2_scale,
                   topk_ids, ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales,
                   w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream);
+}
+
+PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float* x_scale,
+                                   const void* topk_ids, int ids_type, const float* topk_w, int T,
+                                   int K, int E, int H, int I, int N1, int expert_offset,
+                                   const void* w1_codes, const void* w1_scales,
+                                   const float* w1_alpha, const void* w2_codes,
+                                   const void* w2_scales, const float* w2_alpha, int act,
+                                   const pmoe_moe_options* options, void* ws, size_t ws_bytes,
+                                   void* out, void* stream) {
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr};
+  if (options) o = *options;
+  if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
+      o.recipe != PMOE_RECIPE_W4A16)
+    return fail(PMOE_ERR_ARG, "unknown recipe");
+  if (o.finalize != PMOE_FINALIZE_ORDERED && o.finalize != PMOE_FINALIZE_FUSED)
+    return fail(PMOE_ERR_ARG, "unknown finalize mode");
+  if (o.swiglu_limit != 0.0f && act != PMOE_ACT_SWIGLU)
+    return fail(PMOE_ERR_ARG, "swiglu_limit needs the SwiGLU activation");
+  if (o.recipe != PMOE_RECIPE_PER_TENSOR && o.a2_scale)
+    return fail(PMOE_ERR_ARG, "a2_scale belongs to the per-tensor recipe");
+  const Recipe rc = static_cast<Recipe>(o.recipe);
+  return moe_path(rc, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, x_sf,
+                  rc == kPerToken ? x_scale : nullptr, o.a2_scale, topk_ids, ids_type, topk_w, T, K,
+                  E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha, w2_codes, w2_scales,
+                  w2_alpha, act, ws, ws_bytes, out, stream, o.finalize == PMOE_FINALIZE_FUSED,
+                  o.swiglu_limit);
+}
+
+PMOE_EXPORT int pmoe_router_topk(const float* logits, int T, int E, int K, int renormalize,
+                                 int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
+  if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
+  if (K < 1 || K > 32 || K > E) return fail(PMOE_ERR_SHAPE, "K must be in [1, min(32, E)]");
+  if (renormalize != 0 && renormalize != 1) return fail(PMOE_ERR_ARG, "renormalize must be 0 or 1");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  PMOE_TRY(check_ptr(logits, 4, "logits"));
+  PMOE_TRY(check_ptr(topk_ids, 4, "topk_ids"));
+  PMOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  PMOE_HIP(launch_router_topk(logits, T, E, K, renormalize, topk_ids, topk_w,
+                              static_cast<hipStream_t>(stream)));
+  return ok();
 }
 
 PMOE_EXPORT int pmoe_routed_moe_w4a16(const void* x, const void* topk_ids, int ids_type,

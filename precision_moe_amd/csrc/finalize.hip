@@ -51,4 +51,44 @@ hipError_t launch_finalize(const uint16_t* z, const int* row_of_route, const flo
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- fused finalize
+// The order-free finalize accumulates fp32(w * z) of every route with FP32
+// atomic adds inside FC2 (the non-deterministic mode the two-stage finalize
+// replaces); these two kernels clear the accumulator before FC2 and round it
+// to BF16 after. A plain fill kernel rather than a memset keeps the sequence
+// safe to capture in a graph. n is a multiple of 8 (H is a multiple of 64).
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long n4) {
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
+    p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* __restrict__ in, long n8,
+                                                          uint4* __restrict__ out) {
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    const float4 a = in[2 * i], b = in[2 * i + 1];
+    uint4 o;
+    o.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+    o.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+    o.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
+    o.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+    out[i] = o;
+  }
+}
+
+static int stream_grid(long items) {
+  const long g = (items + 255) / 256;
+  return (int)(g < 4096 ? (g > 0 ? g : 1) : 4096);
+}
+
+hipError_t launch_fill_zero(float* p, long n, hipStream_t s) {
+  fill_zero_kernel<<<stream_grid(n / 4), 256, 0, s>>>(reinterpret_cast<float4*>(p), n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* in, long n, uint16_t* out, hipStream_t s) {
+  f32_to_bf16_kernel<<<stream_grid(n / 8), 256, 0, s>>>(reinterpret_cast<const float4*>(in), n / 8,
+                                                        reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
 }  // namespace pmoe

@@ -28,7 +28,9 @@
 // Epilogue: y = acc * fp32(g_row * alpha_e) (scales applied after
 // accumulation, never folded into decoded values), then
 //   FC1 squared ReLU: h = max(y, 0)^2;  FC1 SwiGLU: h = silu(gate) * up (gate
-//   and up column blocks of one output sit in the same wave);  FC2: bf16(y).
+//   and up column blocks of one output sit in the same wave), optionally with
+//   the clamp gate <= L, -L <= up <= L;  FC2: bf16(y);  FC2 with the fused
+//   finalize: FP32 atomic add of w * y into the token's row (order-free).
 //
 // Batch invariance: every output element is one chain of MFMAs over k in fixed
 // order whatever T, the tile or the other rows are; no split-K.
@@ -325,11 +327,22 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       } else if constexpr (MODE == kFc1Swiglu) {
         // p0 is even: block p0 holds gate rows, p0 + 1 the matching up rows.
         if (use0) {
-          const float g = c0[r] * s;
-          const float u = c1[r] * s;
+          float g = c0[r] * s;
+          float u = c1[r] * s;
+          if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
+            g = __builtin_fminf(g, P.swiglu_limit);
+            u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
+          }
           const float silu = g / (1.0f + expf(-g));
           store_h(orow + kColBlock * (p0 >> 1) + n, silu * u);
         }
+      } else if constexpr (MODE == kFc2Fused) {
+        // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
+        const int f = P.out_route[row0 + m];
+        const float wgt = P.out_w[f];
+        float* acc = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
+        if (use0) unsafeAtomicAdd(acc + kColBlock * p0 + n, wgt * (c0[r] * s));
+        if (use1) unsafeAtomicAdd(acc + kColBlock * (p0 + 1) + n, wgt * (c1[r] * s));
       } else {
         uint16_t* out = static_cast<uint16_t*>(P.out) + orow;
         if (use0) out[kColBlock * p0 + n] = (uint16_t)f32_to_bf16(c0[r] * s);
@@ -387,12 +400,14 @@ hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s) {
       case kFc1Relu2: fc_kernel<kFc1Relu2, 1><<<grid, kThreads, 0, s>>>(p); break;
       case kFc1Swiglu: fc_kernel<kFc1Swiglu, 1><<<grid, kThreads, 0, s>>>(p); break;
       case kFc2: fc_kernel<kFc2, 1><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc2Fused: fc_kernel<kFc2Fused, 1><<<grid, kThreads, 0, s>>>(p); break;
     }
   } else {
     switch (mode) {
       case kFc1Relu2: fc_kernel<kFc1Relu2, 0><<<grid, kThreads, 0, s>>>(p); break;
       case kFc1Swiglu: fc_kernel<kFc1Swiglu, 0><<<grid, kThreads, 0, s>>>(p); break;
       case kFc2: fc_kernel<kFc2, 0><<<grid, kThreads, 0, s>>>(p); break;
+      case kFc2Fused: fc_kernel<kFc2Fused, 0><<<grid, kThreads, 0, s>>>(p); break;
     }
   }
   return hipGetLastError();

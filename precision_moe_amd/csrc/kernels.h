@@ -49,7 +49,7 @@ hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_o
                         const RouteBuffers& b, hipStream_t s);
 
 // ---------------------------------------------------------------- grouped GEMMs
-enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2 };
+enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2, kFc2Fused = 3 };
 
 struct FcParams {
   const uint8_t* a_codes;    // A rows of Kd/2 bytes (packed E2M1), or of 2*Kd bytes (BF16)
@@ -68,8 +68,12 @@ struct FcParams {
   const int* expert_offsets;
   const int* counters;       // [1] = number of M-tiles
   int max_tiles;
-  void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z
+  void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z;
+                             // FC2 fused: float accumulator [T][out_stride]
   int out_stride;
+  float swiglu_limit;        // FC1 SwiGLU clamp limit, 0 = none
+  const int* out_route;      // FC2 fused: route of each expert-sorted row
+  const float* out_w;        // FC2 fused: routing weights [T*K]
 };
 __host__ __device__ int fc_col_tiles(int NB);
 hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s);
@@ -77,5 +81,12 @@ hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s);
 // ---------------------------------------------------------------- finalize
 hipError_t launch_finalize(const uint16_t* z, const int* row_of_route, const float* w, int T,
                            int K, int H, uint16_t* out, hipStream_t s);
+// Fused finalize: zero the FP32 accumulator [n] before FC2, round it to BF16 after.
+hipError_t launch_fill_zero(float* p, long n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* in, long n, uint16_t* out, hipStream_t s);
+
+// ---------------------------------------------------------------- router
+hipError_t launch_router_topk(const float* logits, int T, int E, int K, int renorm, int* ids,
+                              float* w, hipStream_t s);
 
 }  // namespace pmoe

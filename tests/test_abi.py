@@ -37,6 +37,9 @@ def test_binding_constants_match_header():
     assert (c["PMOE_ACT_RELU2"], c["PMOE_ACT_SWIGLU"]) == (pm.ACT_RELU2, pm.ACT_SWIGLU)
     assert (c["PMOE_IDS_INT32"], c["PMOE_IDS_INT64"]) == (pm.IDS_INT32, pm.IDS_INT64)
     assert c["PMOE_WS_NUM_FIELDS"] == len(pm.WS_FIELDS)
+    assert (c["PMOE_RECIPE_PER_TOKEN"], c["PMOE_RECIPE_PER_TENSOR"], c["PMOE_RECIPE_W4A16"]) == \
+        (pm.RECIPE_PER_TOKEN, pm.RECIPE_PER_TENSOR, pm.RECIPE_W4A16)
+    assert (c["PMOE_FINALIZE_ORDERED"], c["PMOE_FINALIZE_FUSED"]) == (pm.FINALIZE_ORDERED, pm.FINALIZE_FUSED)
     fields = sorted((v, k) for k, v in c.items() if k.startswith("PMOE_WS_") and k != "PMOE_WS_NUM_FIELDS")
     assert [k[len("PMOE_WS_"):].lower() for _, k in fields] == list(pm.WS_FIELDS)
 
@@ -110,3 +113,31 @@ def test_no_device_is_reported_not_crashed():
     rc = pm.lib().pmoe_quantize_input_per_token(None, 4, 256, None, None, None, None)
     assert rc == 1
     assert "gfx950" in pm.lib().pmoe_last_error().decode() or "device" in pm.lib().pmoe_last_error().decode()
+
+
+def test_options_and_router_validation():
+    lib = pm.lib()
+    base = [None, None, None, None, 0, None, 8, 2, 4, 256, 128, 256, 0] + [None] * 6 + [1]
+    tail = [None, 0, None, None]
+
+    def ex(**kw):
+        o = pm.MoeOptions(kw.get("recipe", 0), kw.get("finalize", 0), kw.get("limit", 0.0), None)
+        return lib.pmoe_routed_moe_ex(*base, ctypes.byref(o), *tail)
+
+    assert ex(recipe=3) == 7                    # unknown recipe
+    assert ex(finalize=2) == 7                  # unknown finalize mode
+    assert ex(limit=-1.0) == 7                  # negative clamp limit
+    relu = list(base)
+    relu[11], relu[19] = 128, 0                 # squared ReLU cannot take a SwiGLU clamp
+    o = pm.MoeOptions(0, 0, 10.0, None)
+    assert lib.pmoe_routed_moe_ex(*relu, ctypes.byref(o), *tail) == 7
+    z = list(base)
+    z[6] = 0                                    # T == 0: no-op with any valid options
+    assert lib.pmoe_routed_moe_ex(*z, ctypes.byref(pm.MoeOptions(2, 1, 5.0, None)), *tail) == 0
+    assert lib.pmoe_routed_moe_ex(*z, None, *tail) == 0
+    assert lib.pmoe_router_topk(None, 0, 64, 6, 0, None, None, None) == 0
+    assert lib.pmoe_router_topk(None, 4, 64, 0, 0, None, None, None) == 3
+    assert lib.pmoe_router_topk(None, 4, 4, 6, 0, None, None, None) == 3
+    assert lib.pmoe_router_topk(None, 4, 2000, 6, 0, None, None, None) == 3
+    assert lib.pmoe_router_topk(None, 4, 64, 6, 2, None, None, None) == 7
+    assert lib.pmoe_quantize_input_per_tensor(None, 4, 100, None, None, None, None) == 3

@@ -1,0 +1,153 @@
+"""GPU parity of the layer steps: the router front, the SwiGLU clamp, the fused
+(order-free) finalize, and pmoe_routed_moe_ex.
+
+Bit-exact: router ids; pmoe_routed_moe_ex with default options equals
+pmoe_routed_moe. Tolerance: router weights to 1e-5 relative (expf and the sum
+order differ from the oracle's float64 softmax); MoE outputs per token
+max |gpu - oracle| <= 1e-2 * max |oracle| and global cosine >= 0.999.
+"""
+import numpy as np
+import pytest
+
+import synth
+from helpers import bf16_bits, dev, dev_bf16
+from oracle import layer as ol
+from oracle import moe as om
+from oracle import quant as oq
+from oracle import recipes as orc
+from oracle.formats import bf16_to_f32
+
+pytestmark = pytest.mark.gpu
+REL_TOL = 1e-2
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def pm():
+    import torch
+    import precision_moe_amd as pm
+    assert torch.cuda.is_available()
+    return pm
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _assert_rows_close(got_bits, want_bits, what):
+    got = bf16_to_f32(got_bits).astype(np.float64)
+    want = bf16_to_f32(want_bits).astype(np.float64)
+    scale = np.abs(want).max(axis=1)
+    err = np.abs(got - want).max(axis=1)
+    bad = np.nonzero(err > REL_TOL * scale)[0]
+    assert bad.size == 0, f"{what}: rows {bad[:8]} rel err {(err / np.maximum(scale, 1e-30))[bad[:8]]}"
+    cos = np.sum(got * want) / (np.linalg.norm(got) * np.linalg.norm(want) + 1e-300)
+    assert cos >= 0.999, f"{what}: cosine {cos}"
+
+
+# ----------------------------------------------------------------------------- router
+def _router_cases():
+    rng = np.random.default_rng(51)
+    cases = []
+    for name in ("tiny", "swiglu", "ep4_t1024", "large"):
+        w = synth.WORKLOADS[name]
+        cases.append((name, synth.router_logits(w), w.K, w.renormalize))
+    lg = rng.standard_normal((300, 1024)).astype(F32)
+    lg[:50, ::7] = 2.5                            # many exact ties at the top
+    lg[50:60] = 0.0                               # all equal
+    cases.append(("E1024_K32_ties", lg, 32, False))
+    cases.append(("E5_K5", rng.standard_normal((33, 5)).astype(F32), 5, True))
+    cases.append(("E65_K1", rng.standard_normal((257, 65)).astype(F32), 1, False))
+    return cases
+
+
+@pytest.mark.parametrize("case", _router_cases(), ids=lambda c: c[0])
+def test_router_topk(pm, case):
+    _, lg, K, renorm = case
+    ids, w = pm.router_topk(dev(lg), K, renorm)
+    _sync()
+    oid, ow = ol.router_topk(lg, K, renorm)
+    assert np.array_equal(ids.cpu().numpy(), oid)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-30)
+
+
+def test_router_feeds_the_path(pm):
+    """Router front + per-token path on the EP4 share: same routing as the seeded inputs."""
+    w = synth.WORKLOADS["ep4_t512"]
+    ids, wts = pm.router_topk(dev(synth.router_logits(w)), w.K, w.renormalize)
+    _sync()
+    sid, swt = synth.router(w)
+    assert np.array_equal(ids.cpu().numpy(), sid)
+    np.testing.assert_allclose(wts.cpu().numpy(), swt, rtol=1e-5)
+
+
+# ----------------------------------------------------------------------------- options
+class ExRun:
+    def __init__(self, pm, w, recipe="per_token", finalize="ordered", limit=0.0, P=None):
+        import torch
+        self.x = synth.activations(w)
+        self.ids, self.wts = synth.router(w)
+        self.P = P or pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+        K = self.ids.shape[1]
+        self.ws = torch.empty(pm.moe_workspace_bytes(w.T, K, w.E, w.H, w.I, self.P.act),
+                              dtype=torch.uint8, device="cuda")
+        xd = dev_bf16(self.x)
+        if recipe == "per_token":
+            xq, xs, xg = pm.quantize_input_per_token(xd)
+        else:
+            xq, xs, xg = xd, None, None
+        self.out = pm.routed_moe_ex(xq, xs, xg, dev(self.ids), dev(self.wts), self.P, recipe=recipe,
+                                    finalize=finalize, swiglu_limit=limit, workspace=self.ws)
+        _sync()
+        self.views = pm.workspace_views(self.ws, w.T, K, w.E, w.H, w.I, self.P.act)
+
+
+def _oracle(w, x, ids, wts, recipe="per_token", **kw):
+    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    xin = oq.quantize_input_per_token(x) if recipe == "per_token" else x
+    return orc.routed_moe_recipe(recipe, xin, ids, wts, W, w.act, **kw)
+
+
+def test_ex_defaults_equal_routed_moe(pm):
+    import torch
+    w = synth.WORKLOADS["swiglu"]
+    run = ExRun(pm, w)
+    xq, xs, xg = pm.quantize_input_per_token(dev_bf16(run.x))
+    ref = pm.routed_moe(xq, xs, xg, dev(run.ids), dev(run.wts), run.P)
+    _sync()
+    assert torch.equal(ref.view(torch.int16), run.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,limit", [("swiglu", 0.05), ("ep4_t512", 0.5)])
+def test_swiglu_clamp(pm, name, limit):
+    w = synth.WORKLOADS[name]
+    run = ExRun(pm, w, limit=limit)
+    experts = None if name == "swiglu" else [0, 17]
+    res = _oracle(w, run.x, run.ids, run.wts, swiglu_limit=limit, experts=experts)
+    rows = np.nonzero(res.computed_rows)[0]
+    h = run.views["h"].cpu().numpy()[rows]
+    assert np.abs(h).max() <= max(limit, 0.2785) * limit * (1 + 1e-5)   # |silu(min(g,L))| * L
+    assert np.all(np.abs(h - res.h[rows]).max(axis=1) <= 1e-4 * np.abs(res.h[rows]).max(axis=1) + 1e-30)
+    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
+    unclamped = _oracle(w, run.x, run.ids, run.wts, experts=experts)
+    assert not np.array_equal(unclamped.z[rows], res.z[rows])       # the clamp bites here
+    if experts is None:
+        _assert_rows_close(bf16_bits(run.out), res.out, "out")
+
+
+@pytest.mark.parametrize("name,recipe", [("tiny", "per_token"), ("swiglu", "per_token"),
+                                         ("swiglu", "w4a16"), ("relu2", "per_token")])
+def test_fused_finalize(pm, name, recipe):
+    w = synth.WORKLOADS[name]
+    run = ExRun(pm, w, recipe=recipe, finalize="fused")
+    orecipe = "weight_only" if recipe == "w4a16" else recipe
+    toks = None if w.T <= 256 else [0, 1, 500, w.T - 1]
+    res = _oracle(w, run.x, run.ids, run.wts, recipe=orecipe, finalize_mode="fused", tokens=toks)
+    got = bf16_bits(run.out)
+    if toks is None:
+        _assert_rows_close(got, res.out, "out (fused)")
+    else:
+        _assert_rows_close(got[toks], res.out[toks], "out (fused)")
+    ordered = ExRun(pm, w, recipe=recipe, P=run.P).out
+    _assert_rows_close(got, bf16_bits(ordered), "fused vs ordered")
