@@ -226,9 +226,22 @@ def main():
     def step_w4a16():
         pm.routed_moe_w4a16(x, ids, wts, P, workspace=ws, out=out)
 
+    def step_fused():
+        pm.quantize_input_per_token(x, out=(xq, xs, xg))
+        pm.routed_moe_ex(xq, xs, xg, ids, wts, P, finalize="fused", workspace=ws, out=out)
+
+    logits = torch.from_numpy(synth.router_logits(w)).to(dev)
+    r_ids = torch.empty_like(ids)
+    r_w = torch.empty_like(wts)
+
+    def step_router():
+        pm.router_topk(logits, w.K, w.renormalize, out=(r_ids, r_w))
+
     recipes = {}
     flops_step = 2.0 * R_rows * (w.N1 * w.H + w.H * w.I)
-    for name, fn in (("per_tensor", step_per_tensor), ("weight_only_w4a16", step_w4a16)):
+    for name, fn in (("per_tensor", step_per_tensor), ("weight_only_w4a16", step_w4a16),
+                     ("per_token_ordered_finalize", step), ("per_token_fused_finalize", step_fused),
+                     ("router_topk", step_router)):
         for _ in range(max(args.warmup // 2, 2)):
             fn()
         torch.cuda.synchronize()
@@ -239,9 +252,13 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        recipes[name] = {"ms_per_step": ms, "tokens/s": T / (ms * 1e-3),
-                         "TFLOP/s": flops_step / (ms * 1e-3) / 1e12}
+        recipes[name] = {"ms_per_step": ms, "tokens/s": T / (ms * 1e-3)}
+        if name != "router_topk":
+            recipes[name]["TFLOP/s"] = flops_step / (ms * 1e-3) / 1e12
         log(f"[bench] {name}: {ms * 1e3:.1f} us/step")
+    # the fixed-order finalize's cost over the order-free one (same inputs, same process)
+    recipes["determinism_cost"] = (recipes["per_token_ordered_finalize"]["ms_per_step"] /
+                                   recipes["per_token_fused_finalize"]["ms_per_step"] - 1.0)
     del P_pt
     counts = np.diff(views["expert_offsets"].cpu().numpy())
     R = int(counts.sum())
