@@ -76,6 +76,22 @@ __device__ __forceinline__ uint32_t e2m1_encode(float q) {
 //   q_i = E2M1(fp32(x_i / e)) if e > 0 else 0.
 // Returns the scale byte; codes go to lo (elements 0..7) and hi (8..15),
 // element 2i in the low nibble of byte i.
+// The E2M1 code of every q = fp32(x / e) of a block, packed low nibble first.
+// Fast form: q is approximated by y = fp32(x * fp32(1 / e)), which is within
+// 3 ulp of q, and encoded by the hardware FP32 -> E2M1 conversion (scale 1.0:
+// round to nearest, ties to the even code, saturating at 6, sign from the
+// IEEE sign; checked against e2m1_encode over every non-NaN FP32 input). Every
+// code boundary (0.25, 0.75, ..., 5) has at most 3 significant bits, so y can
+// round differently from q only when its low 21 mantissa bits sit within 4 of
+// such a value; then the block takes the exact division, as it does when
+// 1 / e overflows.
+__device__ __forceinline__ uint32_t e2m1_pack4(float a, float b, float c, float d) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, 1.0f, 1);
+}
+__device__ __forceinline__ bool near_code_boundary(float y) {
+  return ((__float_as_uint(y) + 4u) & 0x1FFFFFu) <= 8u;
+}
 __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g, uint32_t& lo,
                                                   uint32_t& hi) {
   float amax_b = 0.0f;
@@ -91,10 +107,22 @@ __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g,
   lo = 0;
   hi = 0;
   if (e > 0.0f) {
+    const float r = 1.0f / e;
+    float y[16];
+    bool exact = !(r <= 3.4e38f);  // 1 / e overflowed
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(x[i] / e) << (4 * i);
+    for (int i = 0; i < 16; ++i) {
+      y[i] = x[i] * r;
+      exact |= near_code_boundary(y[i]);
+    }
+    if (exact) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(x[8 + i] / e) << (4 * i);
+      for (int i = 0; i < 16; ++i) y[i] = x[i] / e;
+    }
+    lo = e2m1_pack4(y[0], y[1], y[2], y[3]) |
+         (e2m1_pack4(y[4], y[5], y[6], y[7]) << 16);
+    hi = e2m1_pack4(y[8], y[9], y[10], y[11]) |
+         (e2m1_pack4(y[12], y[13], y[14], y[15]) << 16);
   }
   return sf;
 }

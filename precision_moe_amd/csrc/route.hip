@@ -87,10 +87,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ bloc
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < NB; ++b) {
-      const int c = block_counts[(long)b * E + e];
-      block_counts[(long)b * E + e] = total;  // exclusive prefix over blocks
-      total += c;
+    // exclusive prefix over blocks, in place; eight independent loads per
+    // round so the latency is paid once per eight blocks, not once per block
+    for (int b0 = 0; b0 < NB; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = b0 + i < NB ? block_counts[(long)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b0 + i < NB) block_counts[(long)(b0 + i) * E + e] = total;
+        total += c[i];
+      }
     }
   }
   const int incl = block_inclusive_scan_1024(total, sh);
