@@ -164,30 +164,30 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # The step is issued as three calls so that HIP events on the launch stream
-    # bracket the FC1 kernel inside the timed region (an event costs ~nothing on
-    # the GPU); the roofline figure uses their average.
-    def timed_step(ev_a, ev_b):
-        pm.quantize_input_per_token(x, out=(xq, xs, xg))
-        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_ROUTE, pm.STEP_ROUTE))
-        ev_a.record()
-        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_FC1, pm.STEP_FC1))
-        ev_b.record()
-        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_REQUANT, pm.STEP_FINALIZE))
-
-    fc1_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        timed_step(*fc1_evs[i])
+    for _ in range(args.steps):
+        step()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    fc1_ms_timed = float(np.mean([a.elapsed_time(b) for a, b in fc1_evs]))
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # ---------------------------------------------------------------- FC1 alone
+    # Inside a step the two expert halves run FC1 on two streams, overlapped
+    # with the other half's work; the roofline figure times the whole FC1
+    # kernel (one launch over all experts, the same code) with HIP events on
+    # the stream it runs on, over as many launches as the timed region had.
+    fc1_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for a, b in fc1_evs:
+        a.record()
+        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_FC1, pm.STEP_FC1))
+        b.record()
+    torch.cuda.synchronize()
+    fc1_ms_timed = float(np.mean([a.elapsed_time(b) for a, b in fc1_evs]))
 
     # ---------------------------------------------------------------- per-step events
     names = ["quantize", "route", "fc1", "requant", "fc2", "finalize"]
@@ -226,6 +226,10 @@ def main():
     def step_w4a16():
         pm.routed_moe_w4a16(x, ids, wts, P, workspace=ws, out=out)
 
+    def step_one_stream():
+        pm.quantize_input_per_token(x, out=(xq, xs, xg))
+        pm.routed_moe_ex(xq, xs, xg, ids, wts, P, streams=1, workspace=ws, out=out)
+
     def step_fused():
         pm.quantize_input_per_token(x, out=(xq, xs, xg))
         pm.routed_moe_ex(xq, xs, xg, ids, wts, P, finalize="fused", workspace=ws, out=out)
@@ -240,7 +244,8 @@ def main():
     recipes = {}
     flops_step = 2.0 * R_rows * (w.N1 * w.H + w.H * w.I)
     for name, fn in (("per_tensor", step_per_tensor), ("weight_only_w4a16", step_w4a16),
-                     ("per_token_ordered_finalize", step), ("per_token_fused_finalize", step_fused),
+                     ("per_token_ordered_finalize", step), ("per_token_one_stream", step_one_stream),
+                     ("per_token_fused_finalize", step_fused),
                      ("router_topk", step_router)):
         for _ in range(max(args.warmup // 2, 2)):
             fn()

@@ -4,6 +4,11 @@
  * C ABI. Every compute entry point enqueues HIP kernels on the caller's stream
  * (`stream` is a hipStream_t; NULL means the legacy default stream), returns a
  * status code, and never allocates device memory, synchronizes, or aborts.
+ * The routed-MoE entry points may also enqueue work on one library-owned
+ * stream per device (created on first use, default priority, kept until the
+ * process ends), forked from and joined back into the caller's stream with
+ * events, so the call stays ordered on the caller's stream and can be captured
+ * in a graph.
  * All tensors are caller-owned device buffers (the library keeps no pointer to
  * them after the call returns and caches nothing about them). All checks run on
  * the host before the first launch; when a call returns an error, no kernel was
@@ -321,6 +326,9 @@ typedef struct pmoe_moe_options {
   int finalize;           /* PMOE_FINALIZE_*                                                */
   float swiglu_limit;     /* > 0: SwiGLU clamp, gate <= L and -L <= up <= L; 0: none         */
   const float* a2_scale;  /* per-tensor recipe: device float32 scalar; otherwise NULL       */
+  int streams;            /* 0: automatic; 1: one stream; 2: the two halves of the experts
+                             run FC1 -> requant -> FC2 on the caller's stream and on a second
+                             stream, joined before the finalize (same bits either way)   */
 } pmoe_moe_options;
 
 /*
@@ -340,6 +348,7 @@ typedef struct pmoe_moe_options {
  *   swiglu_limit : the clamp of [FlashInfer #5019 . Tensor and numerical
  *                  contract, 'Compute order']; PMOE_ERR_ARG unless act is
  *                  SwiGLU (or the limit is 0).
+ *   streams      : see the struct; automatic means two streams once T*K >= 2048.
  * Other arguments, layout and errors as the recipe's own entry point.
  */
 int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float* x_scale,

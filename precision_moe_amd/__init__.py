@@ -31,7 +31,8 @@ _i = ctypes.c_int
 class MoeOptions(ctypes.Structure):
     """pmoe_moe_options (include/pmoe.h)."""
     _fields_ = [("recipe", ctypes.c_int), ("finalize", ctypes.c_int),
-                ("swiglu_limit", ctypes.c_float), ("a2_scale", ctypes.c_void_p)]
+                ("swiglu_limit", ctypes.c_float), ("a2_scale", ctypes.c_void_p),
+                ("streams", ctypes.c_int)]
 _SIGNATURES = {
     "pmoe_version": (_i, []),
     "pmoe_last_error": (ctypes.c_char_p, []),
@@ -362,7 +363,7 @@ def routed_moe_w4a16(x, topk_ids, topk_w, weights: PreparedWeights, act=None, ex
 
 def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, recipe="per_token",
                   finalize="ordered", swiglu_limit=0.0, a2=None, act=None, expert_offset=0,
-                  workspace=None, out=None, stream=None):
+                  workspace=None, out=None, stream=None, streams=0):
     """The routed path with options (pmoe_routed_moe_ex): recipe "per_token" (x = xq, x_sf,
     x_scale), "per_tensor" (x = xq, x_sf; a2) or "w4a16" (x = BF16 activations; x_sf, x_scale
     None); finalize "ordered" or "fused"; swiglu_limit > 0 clamps SwiGLU."""
@@ -374,7 +375,7 @@ def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, 
         x = _bf16_storage(x.contiguous())
     workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
     opt = MoeOptions(_RECIPES[recipe], _FINALIZE[finalize], float(swiglu_limit),
-                     _f32_scalar(a2).data_ptr() if a2 is not None else None)
+                     _f32_scalar(a2).data_ptr() if a2 is not None else None, int(streams))
     _check(lib().pmoe_routed_moe_ex(
         _ptr(x), _ptr(x_sf), _ptr(x_scale), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H,
         W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),

@@ -285,7 +285,7 @@ PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, v
   PMOE_TRY(check_ptr(hq, 16, "hq"));
   PMOE_TRY(check_ptr(h_sf, 4, "h_sf"));
   PMOE_TRY(check_ptr(h_scale, 4, "h_scale"));
-  PMOE_HIP(launch_quantize_f32(h, R, nullptr, L, nullptr, static_cast<uint8_t*>(hq),
+  PMOE_HIP(launch_quantize_f32(h, R, nullptr, nullptr, L, nullptr, static_cast<uint8_t*>(hq),
                                static_cast<uint8_t*>(h_sf), h_scale, static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -309,6 +309,33 @@ namespace {
 enum Recipe { kPerToken = PMOE_RECIPE_PER_TOKEN, kPerTensor = PMOE_RECIPE_PER_TENSOR,
               kW4A16 = PMOE_RECIPE_W4A16 };
 
+// A second stream and a fork / join event pair per device, created on first
+// use and kept until the process ends: the two halves of the experts run their
+// FC1 -> requant -> FC2 chains concurrently, so each chain's launch tail is
+// filled with the other's work. Default stream priority. The mutex keeps each
+// call's record / wait pairs together when several host threads enqueue on
+// the same device.
+struct Aux {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_aux_mu;
+Aux g_aux[64];
+
+int aux_for_current_device(Aux** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(PMOE_ERR_DEVICE, "no usable current device");
+  Aux& a = g_aux[dev];
+  if (!a.s2) {
+    PMOE_HIP(hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking));
+    PMOE_HIP(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
+    PMOE_HIP(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+  }
+  *out = &a;
+  return PMOE_OK;
+}
+
 // Steps first..last of the routed path under one recipe.
 //   per-token : x = xq, x_sf, x_scale (per-token NVFP4); requant per row.
 //   per-tensor: x = xq, x_sf (static scale folded into the alphas); x_scale
@@ -321,7 +348,8 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
              int E, int H, int I, int N1, int expert_offset, const void* w1_codes,
              const void* w1_scales, const float* w1_alpha, const void* w2_codes,
              const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
-             void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f) {
+             void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f,
+             int streams = 0) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
   if (!(swiglu_limit >= 0.0f)) return fail(PMOE_ERR_ARG, "swiglu_limit must be >= 0");
@@ -400,11 +428,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p1.swiglu_limit = swiglu_limit;
   p1.out_route = nullptr;
   p1.out_w = nullptr;
-  if (run(PMOE_STEP_FC1)) PMOE_HIP(launch_fc(act == PMOE_ACT_SWIGLU ? kFc1Swiglu : kFc1Relu2, p1, s));
-
-  if (run(PMOE_STEP_REQUANT) && rc != kW4A16)
-    PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, rb.counters, I,
-                                 rc == kPerTensor ? a2 : nullptr, hq, h_sf, h_scale, s));
+  p1.part = 0;
 
   FcParams p2 = p1;
   p2.a_codes = bf16_a ? static_cast<const uint8_t*>(h) : hq;
@@ -425,9 +449,40 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     p2.out_route = rb.route_of_row;
     p2.out_w = topk_w;
   }
-  if (run(PMOE_STEP_FC2)) {
-    if (fused) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
-    PMOE_HIP(launch_fc(fused ? kFc2Fused : kFc2, p2, s));
+  const FcMode m1 = act == PMOE_ACT_SWIGLU ? kFc1Swiglu : kFc1Relu2;
+  const FcMode m2 = fused ? kFc2Fused : kFc2;
+  const float* static_a2 = rc == kPerTensor ? a2 : nullptr;
+
+  // FC1 -> requant -> FC2 of one part of the experts on one stream.
+  auto chain = [&](int part, hipStream_t st, bool fc1, bool requant, bool fc2) -> int {
+    FcParams q1 = p1, q2 = p2;
+    q1.part = q2.part = part;
+    const int* row_begin = part == 2 ? rb.counters + 3 : nullptr;
+    const int* row_end = part == 1 ? rb.counters + 3 : rb.counters;
+    if (fc1) PMOE_HIP(launch_fc(m1, q1, st));
+    if (requant && rc != kW4A16)
+      PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, row_begin, row_end, I,
+                                   static_a2, hq, h_sf, h_scale, st));
+    if (fc2) PMOE_HIP(launch_fc(m2, q2, st));
+    return PMOE_OK;
+  };
+  if (fused && run(PMOE_STEP_FC2)) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+  // Two streams for the whole FC1..FC2 range when asked (streams == 2) or by
+  // default (streams == 0) once there is enough work to fill the GPU twice.
+  const bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
+                     (streams == 2 || (streams == 0 && TK >= 2048));
+  if (split) {
+    Aux* aux = nullptr;
+    PMOE_TRY(aux_for_current_device(&aux));
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    PMOE_HIP(hipEventRecord(aux->fork, s));
+    PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
+    PMOE_TRY(chain(1, s, true, true, true));
+    PMOE_TRY(chain(2, aux->s2, true, true, true));
+    PMOE_HIP(hipEventRecord(aux->join, aux->s2));
+    PMOE_HIP(hipStreamWaitEvent(s, aux->join, 0));
+  } else {
+    PMOE_TRY(chain(0, s, run(PMOE_STEP_FC1), run(PMOE_STEP_REQUANT), run(PMOE_STEP_FC2)));
   }
 
   if (run(PMOE_STEP_FINALIZE)) {
@@ -486,7 +541,7 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
                                    const void* w2_scales, const float* w2_alpha, int act,
                                    const pmoe_moe_options* options, void* ws, size_t ws_bytes,
                                    void* out, void* stream) {
-  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr};
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0};
   if (options) o = *options;
   if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
       o.recipe != PMOE_RECIPE_W4A16)
@@ -497,12 +552,13 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
     return fail(PMOE_ERR_ARG, "swiglu_limit needs the SwiGLU activation");
   if (o.recipe != PMOE_RECIPE_PER_TENSOR && o.a2_scale)
     return fail(PMOE_ERR_ARG, "a2_scale belongs to the per-tensor recipe");
+  if (o.streams < 0 || o.streams > 2) return fail(PMOE_ERR_ARG, "streams must be 0, 1 or 2");
   const Recipe rc = static_cast<Recipe>(o.recipe);
   return moe_path(rc, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, x_sf,
                   rc == kPerToken ? x_scale : nullptr, o.a2_scale, topk_ids, ids_type, topk_w, T, K,
                   E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha, w2_codes, w2_scales,
                   w2_alpha, act, ws, ws_bytes, out, stream, o.finalize == PMOE_FINALIZE_FUSED,
-                  o.swiglu_limit);
+                  o.swiglu_limit, o.streams);
 }
 
 PMOE_EXPORT int pmoe_router_topk(const float* logits, int T, int E, int K, int renormalize,

@@ -363,12 +363,15 @@ __global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcPar
   // column tile, then M-tile; XCD x = blockIdx % 8 takes items
   // [x*per, (x+1)*per) in order.
   const int NT = fc_col_tiles(P.NB);
-  const int total = P.counters[1] * NT;
+  // the part's tiles: all, or those of the first / second half of the experts
+  const int t_lo = P.part == 2 ? P.counters[2] : 0;
+  const int t_hi = P.part == 1 ? P.counters[2] : P.counters[1];
+  const int total = (t_hi - t_lo) * NT;
   const int per = (total + 7) >> 3;
   const int j = blockIdx.x >> 3;
   if (j >= per) return;
-  const int item = (blockIdx.x & 7) * per + j;
-  if (item >= total) return;
+  const int item = t_lo * NT + (blockIdx.x & 7) * per + j;
+  if (item >= t_hi * NT) return;
   const int4 ta = reinterpret_cast<const int4*>(P.tiles)[item / NT];  // a tile of the item's expert
   const int first = ta.z, count = ta.w;
   const int local = item - first * NT;

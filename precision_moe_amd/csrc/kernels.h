@@ -23,9 +23,10 @@ constexpr int kMaxRow = 256 * kMaxBlocksPerThread * 16;
 // address of a static scale a (rows use g = 1/a; no scale is written).
 hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
                                 uint8_t* x_sf, float* x_scale, hipStream_t s);
-hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L,
-                               const float* static_a, uint8_t* hq, uint8_t* h_sf, float* h_scale,
-                               hipStream_t s);
+// Rows [*row_begin_dev, *row_end_dev) of R (either pointer may be null: 0 / R).
+hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
+                               const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
+                               uint8_t* h_sf, float* h_scale, hipStream_t s);
 
 // ---------------------------------------------------------------- weights
 int weight_amax_parts(long elems);
@@ -40,7 +41,7 @@ struct RouteBuffers {
   int* block_counts;    // [route blocks][E]
   int* expert_offsets;  // [E+1]
   int* tiles;           // [max_tiles][4] = {expert, first local row, expert's first tile, expert's tiles}
-  int* counters;        // [4] = {R, tiles, 0, 0}
+  int* counters;        // [4] = {R, tiles, tiles of experts < ceil(E/2), rows of those experts}
   int* row_of_route;    // [TK]
   int* route_of_row;    // [TK]
 };
@@ -66,7 +67,8 @@ struct FcParams {
   int KC;                    // chunks of 64 along the reduction
   const int* tiles;          // [tiles][4], see RouteBuffers
   const int* expert_offsets;
-  const int* counters;       // [1] = number of M-tiles
+  const int* counters;       // [1] = number of M-tiles, [2] = M-tiles of the first expert half
+  int part;                  // 0: all experts; 1 / 2: first / second half of the experts
   int max_tiles;
   void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z;
                              // FC2 fused: float accumulator [T][out_stride]

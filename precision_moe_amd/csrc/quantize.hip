@@ -41,19 +41,21 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
   }
 }
 
-// rows: number of rows, or (if rows_dev != nullptr) read from *rows_dev at run
-// time (the intermediate has a device-side count of valid routes).
+// Rows [begin, end): begin = *row_begin_dev (0 if null), end = *row_end_dev
+// (rows if null), read at run time (the intermediate has a device-side count
+// of valid routes). Workgroup b handles row begin + b.
 // static_a: null for per-row scales, else the static scale a (kStatic).
 template <bool kBf16, bool kStatic>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int rows,
-                                                            const int* __restrict__ rows_dev,
+                                                            const int* __restrict__ row_begin_dev,
+                                                            const int* __restrict__ row_end_dev,
                                                             int L, const float* __restrict__ static_a,
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             float* __restrict__ scale) {
   __shared__ float red[4];
-  const long row = blockIdx.x;
-  const int nrows = rows_dev ? *rows_dev : rows;
+  const long row = blockIdx.x + (row_begin_dev ? *row_begin_dev : 0);
+  const int nrows = row_end_dev ? *row_end_dev : rows;
   if (row >= nrows) return;
   const int tid = threadIdx.x;
   const int nblk = L / kBlock;
@@ -102,19 +104,23 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
                                 uint8_t* x_sf, float* x_scale, hipStream_t s) {
   if (static_a)
-    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, H, static_a, xq, x_sf, nullptr);
+    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, static_a, xq, x_sf,
+                                                       nullptr);
   else
-    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, H, nullptr, xq, x_sf, x_scale);
+    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, nullptr, xq, x_sf,
+                                                        x_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_f32(const float* h, int R, const int* rows_dev, int L,
-                               const float* static_a, uint8_t* hq, uint8_t* h_sf, float* h_scale,
-                               hipStream_t s) {
+hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
+                               const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
+                               uint8_t* h_sf, float* h_scale, hipStream_t s) {
   if (static_a)
-    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, rows_dev, L, static_a, hq, h_sf, nullptr);
+    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, static_a,
+                                                        hq, h_sf, nullptr);
   else
-    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, rows_dev, L, nullptr, hq, h_sf, h_scale);
+    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, nullptr,
+                                                         hq, h_sf, h_scale);
   return hipGetLastError();
 }
 

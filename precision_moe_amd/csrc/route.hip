@@ -10,10 +10,12 @@
 //                   the expert id bits + per-wave counts in LDS), and the block's
 //                   per-expert counts.
 //   route_scan    : one workgroup: per expert, exclusive prefix over blocks
-//                   (in place), totals, exclusive scan over experts, and the
+//                   (in place), totals, exclusive scan over experts, the
 //                   M-tile list {expert, first local row, expert's first
 //                   tile, expert's tile count} (tiles of 64 rows, grouped by
-//                   expert in expert order).
+//                   expert in expert order), and where the first half of the
+//                   experts ends in tiles and rows (counters[2], counters[3]),
+//                   for running the two halves on two streams.
 //   route_scatter : row = expert start + block prefix + in-block rank;
 //                   writes row_of_route and route_of_row.
 // A route is valid iff expert_offset <= id < expert_offset + E; other ids
@@ -118,8 +120,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ bloc
     expert_offsets[E] = R;
     counters[0] = R;
     counters[1] = sh[1023];
-    counters[2] = 0;
-    counters[3] = 0;
+  }
+  if (e == (E + 1) / 2) {  // the first expert of the second half (E itself when E == 1)
+    counters[2] = tstart;
+    counters[3] = start;
   }
 }
 

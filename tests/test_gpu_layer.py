@@ -151,3 +151,24 @@ def test_fused_finalize(pm, name, recipe):
         _assert_rows_close(got[toks], res.out[toks], "out (fused)")
     ordered = ExRun(pm, w, recipe=recipe, P=run.P).out
     _assert_rows_close(got, bf16_bits(ordered), "fused vs ordered")
+
+
+@pytest.mark.parametrize("name,recipe", [("relu2", "per_token"), ("ep4_t1024", "per_token"),
+                                         ("ep4_t512", "w4a16")])
+def test_two_streams_same_bits(pm, name, recipe):
+    """The two expert halves on two streams give exactly the one-stream result."""
+    import torch
+    w = synth.WORKLOADS[name]
+    x = dev_bf16(synth.activations(w))
+    ids, wts = (dev(a) for a in synth.router(w))
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    if recipe == "per_token":
+        xin = pm.quantize_input_per_token(x)
+    else:
+        xin = (x, None, None)
+    outs = [pm.routed_moe_ex(*xin, ids, wts, P, recipe=recipe, streams=s) for s in (1, 2, 0, 2)]
+    _sync()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    del P
+    torch.cuda.empty_cache()
