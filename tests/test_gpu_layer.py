@@ -172,3 +172,60 @@ def test_two_streams_same_bits(pm, name, recipe):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     del P
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("recipe,finalize", [("per_token", "ordered"), ("per_token", "fused"),
+                                             ("per_tensor", "ordered"), ("w4a16", "ordered"),
+                                             ("w4a16", "fused")])
+def test_edges_offsets_invalid_routes(pm, recipe, finalize):
+    """expert_offset with int64 ids and -1 fills; a token whose routes are all outside the
+    shard gets +0; results match the same call on shifted int32 ids with offset 0."""
+    import torch
+    w = synth.WORKLOADS["swiglu"]
+    x = synth.activations(w)
+    ids, wts = synth.router(w)
+    ids = ids.astype(np.int64) + 40
+    ids[5, :] = -1                                  # token 5: no route at all
+    ids[9, :] = 7                                   # token 9: every id below the shard
+    ids[12, 1] = 40 + w.E                           # one id just past the shard
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    a2 = torch.tensor([2688.0 / 0.5], dtype=torch.float32, device="cuda")
+    xd = dev_bf16(x)
+    if recipe == "per_token":
+        xin = pm.quantize_input_per_token(xd)
+    elif recipe == "per_tensor":
+        a1 = torch.tensor([float(2688.0 / np.abs(bf16_to_f32(x)).max())], device="cuda")
+        P = pm.prepare_weights(*synth.all_weights(w, device="cuda"), input_scales=(a1, a2))
+        xin = pm.quantize_input_per_tensor(xd, a1) + (None,)
+    else:
+        xin = (xd, None, None)
+    kw = dict(recipe=recipe, finalize=finalize, a2=a2 if recipe == "per_tensor" else None)
+    got = pm.routed_moe_ex(*xin, dev(ids), dev(wts), P, expert_offset=40, **kw)
+    shifted = np.where((ids >= 40) & (ids < 40 + w.E), ids - 40, -1).astype(np.int32)
+    ref = pm.routed_moe_ex(*xin, dev(shifted), dev(wts), P, **kw)
+    _sync()
+    g, r = bf16_bits(got), bf16_bits(ref)
+    assert not g[5].any() and not g[9].any()
+    if finalize == "ordered":
+        assert np.array_equal(g, r)
+    else:
+        _assert_rows_close(np.delete(g, [5, 9], 0), np.delete(r, [5, 9], 0), "fused with offset")
+
+
+def test_edges_single_token_and_router_k_equals_e(pm):
+    import torch
+    w = synth.WORKLOADS["tiny"]
+    x = synth.activations(w, 1)
+    ids, wts = synth.router(w, 1)
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    out = pm.routed_moe_ex(dev_bf16(x), None, None, dev(ids), dev(wts), P, recipe="w4a16")
+    _sync()
+    res = _oracle(w, x, ids, wts, recipe="weight_only")
+    _assert_rows_close(bf16_bits(out), res.out, "T=1 W4A16")
+    lg = synth.router_logits(w, 33)
+    rid, rw = pm.router_topk(dev(lg), w.E, True)
+    _sync()
+    oid, ow = ol.router_topk(lg, w.E, True)
+    assert np.array_equal(rid.cpu().numpy(), oid)
+    np.testing.assert_allclose(rw.cpu().numpy(), ow, rtol=1e-5)
+    np.testing.assert_allclose(rw.cpu().numpy().sum(axis=1), 1.0, rtol=1e-5)
