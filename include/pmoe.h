@@ -85,12 +85,14 @@ const char* pmoe_last_error(void);
  * the tile streams a single sequential region:
  *
  *   codes  (uint8, E*NBp*32*Kd/2 bytes): byte offset
- *            (((((e*NT + ct)*KC + c)*8 + pos)*64 + lane)*16 + j*4 + i/2
- *          holds element k = c*64 + 16*j + 8*(lane/32) + i (nibble i%2, low first)
- *          of row n(p, lane%32), for j in 0..3, i in 0..7.
+ *            (((((e*NT + ct)*KC + c)*8 + pos)*64 + lane)*16 + (2*h + s)*4 + i/2
+ *          holds element k = c*64 + 32*s + 8*(lane/16) + i (nibble i%2, low first)
+ *          of row n(p, 16*h + lane%16), for h, s in 0..1, i in 0..7 (the operand
+ *          order of a 16x16x32 MFMA: lane = column, 8 consecutive k per lane).
  *   scales (uint8, E*NBp*32*Kd/16 bytes): byte offset
- *            ((((e*NT + ct)*KC + c)*8 + pos)*32 + col)*4 + j
- *          holds the E4M3 scale of 16-block (c*4 + j) of row n(p, col).
+ *            ((((e*NT + ct)*KC + c)*8 + pos)*32 + d)*4 + 2*h + s
+ *          holds the E4M3 scale of 16-block (c*4 + 2*s + d/16) of row
+ *          n(p, 16*h + d%16), for d in 0..31.
  *   alpha  (float32, E values).
  *
  * Row map n(p, col): non-gated FC1 and FC2: n = 32*p + col. Gated FC1 (N1 = 2I)

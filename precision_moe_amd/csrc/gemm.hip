@@ -68,15 +68,21 @@ constexpr int kPrefetch = kRing - 1;               // B chunks in flight ahead o
 
 __host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
 
-__device__ __forceinline__ floatx16 mfma32(half8_t a, half8_t b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(half8_t a, half8_t b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx4 mfma16(bf16x8_t a, bf16x8_t b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Four decoded B fragments (k-steps 0..3 of a 64-chunk) of one column block:
-// FP16 for NVFP4 activations (AK = 0), BF16 for BF16 activations (AK = 1).
+// The four decoded B fragments of one prepared position (32 weight rows = two
+// 16-column blocks h) for one 64-element chunk (two 32-element k-steps s):
+// b[2h + s]. FP16 for NVFP4 activations (AK = 0), BF16 for BF16 activations
+// (AK = 1). Lane l holds column l%16 of each block and the 8 elements
+// 32s + 8(l/16) .. +7; its scale dword holds the E4M3 scale of word (h, s) in
+// byte 2h + s.
 template <int AK>
 struct BFrag {
   using V = std::conditional_t<AK == 1, bf16x8_t, half8_t>;
@@ -98,12 +104,12 @@ struct BFrag {
   }
 };
 
-// Main loop + epilogue for one tile. TWO: the tile has more than 32 rows, so
-// both row blocks are computed. Every global load inside the loop is
-// unconditional (addresses past the end are clamped to the last chunk and the
-// data is never used), which keeps the in-order load counters exact so the
-// four-chunk B ring really stays in flight.
-template <int MODE, bool TWO, int AK>
+// Main loop + epilogue for one tile. NRB: the tile's rows rounded up to 16-row
+// blocks (1..4); blocks past it are neither staged nor multiplied. Every global
+// load inside the loop is unconditional (addresses past the end are out of the
+// buffer range and return zeros, and that data is never used), which keeps the
+// in-order load counters exact so the B ring really stays in flight.
+template <int MODE, int NRB, int AK>
 __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
                                         int mrows, int nt) {
@@ -112,10 +118,9 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   const int NB = P.NB, KC = P.KC;
 
   // A stage fill: thread t -> row r = t/4 of the stage, elements 32*(t%4) ..
-  // +32 (k-chunks kk = 4*(t%4) + i), stored at slots kk ^ (r % 16). Rows of a
-  // skipped upper block are not filled (t >= 128 when !TWO). Out-of-range
-  // buffer reads (the empty half of an odd final stage at the last row)
-  // return zeros and are never used.
+  // +32 (k-slots kk = 4*(t%4) + i of 8 elements), stored at slots kk ^ (r % 16).
+  // Rows of skipped 16-row blocks are not filled. Out-of-range buffer reads
+  // (past the last stage at the last row) return zeros and are never used.
   // AK = 0: NVFP4 rows (K/2 bytes of codes + K/16 scales per row), decoded
   // exactly to FP16 on the way into LDS. AK = 1: BF16 rows (2K bytes), copied
   // into LDS as they are (W4A16).
@@ -123,7 +128,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   constexpr int kAQ = AK == 1 ? 4 : 1;             // 16-byte loads per thread and stage
   const int a_row_bytes = AK == 1 ? KC * 128 : KC * 32;
   const int ar = tid >> 2, aq = tid & 3;
-  const bool a_fill = TWO || ar < 32;
+  const bool a_fill = ar < 16 * NRB;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)P.a_codes, (short)0, (int)(P.a_rows * a_row_bytes), kBufFlags);
   const __amdgpu_buffer_rsrc_t a_srsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -163,21 +168,23 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       }
     }
   };
-  // MFMA fragment reads: lane -> row lane%32 (+32 for the upper block), k-chunk
-  // kk = 8*half + 2*j + lane/32 of the stage, at slot kk ^ row%16.
-  int frag[2][4];
+  // MFMA fragment reads: row block rb, lane -> row 16*rb + lane%16, k-slot
+  // kk = 8*half + 4*s + lane/16 of the stage (k-step s of the chunk), at slot
+  // kk ^ row%16 (eight lanes of a 128-byte access hit eight distinct slots).
+  int frag[2][2];
   {
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) frag[hf][j] = r * kLdsRow + (((8 * hf + 2 * j + h) ^ (r & 15)) << 4);
+      for (int st2 = 0; st2 < 2; ++st2) frag[hf][st2] = r * kLdsRow + (((8 * hf + 4 * st2 + g) ^ r) << 4);
   }
 
-  // B stream of this column tile: chunk c of its 8 column blocks is one
-  // contiguous 9 KB slab (8 KB codes + 1 KB scales); wave w reads blocks 2w
-  // and 2w+1 of it. Reads past the last chunk are out of the buffer range and
-  // return zeros. Column blocks past NB (padding of the last tile) hold zeros.
+  // B stream of this column tile: chunk c of its 8 positions (32 weight rows
+  // each) is one contiguous 9 KB slab (8 KB codes + 1 KB scales); wave w reads
+  // positions 2w and 2w+1 of it. Reads past the last chunk are out of the
+  // buffer range and return zeros. Positions past NB (padding of the last
+  // tile) hold zeros.
   const int NT = padded_col_blocks(NB) / kColTileBlocks;
   const int p0 = nt * kColTile + wave * kBlocksPerWave;
   const long tile = (long)e * NT + nt;
@@ -189,7 +196,8 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       kBufFlags);
   const int pos0 = wave * kBlocksPerWave;
   const int bq_voff0 = pos0 * 1024 + lane * 16, bq_voff1 = bq_voff0 + 1024;
-  const int bs_voff0 = pos0 * 128 + (lane & 31) * 4, bs_voff1 = bs_voff0 + 128;
+  const int sdw = (lane & 15) + 16 * (lane >> 5);  // this lane's scale dword of a position
+  const int bs_voff0 = pos0 * 128 + sdw * 4, bs_voff1 = bs_voff0 + 128;
   auto load_q = [&](int voff, int c) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bq, voff, c * (kColTileBlocks * 1024), 0);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -198,7 +206,13 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bs, voff, c * (kColTileBlocks * 128), 0);
   };
 
-  floatx16 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};  // [row block][col block]
+  // acc[rb][cb]: 16-row block rb, 16-column block cb of the wave's 64 columns
+  // (cb = 2 * (position - p0) + h).
+  floatx4 acc[NRB][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // B register ring: chunk c lives in slot c % kRing. Chunk c refills slot
   // (c + kPrefetch) % kRing -- the slot chunk c - 1 has just finished
@@ -230,40 +244,38 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     rs0[r] = load_s(bs_voff0, cn);
     rs1[r] = load_s(bs_voff1, cn);
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 q0 = rq0[i], q1 = rq1[i];
-    const uint32_t sc0 = rs0[i], sc1 = rs1[i];
     using AV = typename BFrag<AK>::V;
-    AV a0[4], a1[4];
+    AV a[NRB][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a0[j] = *reinterpret_cast<const AV*>(abuf + frag[half][j]);
-    if constexpr (TWO) {
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a1[j] = *reinterpret_cast<const AV*>(abuf + 32 * kLdsRow + frag[half][j]);
+      for (int s2 = 0; s2 < 2; ++s2)
+        a[rb][s2] = *reinterpret_cast<const AV*>(abuf + 16 * rb * kLdsRow + frag[half][s2]);
+    {
+      const BFrag<AK> f(rq0[i], rs0[i]);  // column blocks 0, 1 of the wave
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          acc[rb][0] = mfma16(a[rb][s2], f.b[s2], acc[rb][0]);
+          acc[rb][1] = mfma16(a[rb][s2], f.b[2 + s2], acc[rb][1]);
+        }
     }
     {
-      const BFrag<AK> f(q0, sc0);
+      const BFrag<AK> f(rq1[i], rs1[i]);  // column blocks 2, 3
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc00 = mfma32(a0[j], f.b[j], acc00);
-      if constexpr (TWO) {
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc10 = mfma32(a1[j], f.b[j], acc10);
-      }
-    }
-    {
-      const BFrag<AK> f(q1, sc1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc01 = mfma32(a0[j], f.b[j], acc01);
-      if constexpr (TWO) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc11 = mfma32(a1[j], f.b[j], acc11);
-      }
+        for (int rb = 0; rb < NRB; ++rb) {
+          acc[rb][2] = mfma16(a[rb][s2], f.b[s2], acc[rb][2]);
+          acc[rb][3] = mfma16(a[rb][s2], f.b[2 + s2], acc[rb][3]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Full stage st (two chunks) in LDS buffer st % 3 == t, ring slots slot and
-  // slot + 1; loads the next stage's A and stores it into the next buffer.
+  // Full stage st (two chunks) in LDS buffer t, ring slots slot and slot + 1;
+  // loads the next stage's A and stores it into the next buffer.
   auto stage = [&](const int st, const int t, const int slot) {
     ARaw v;
     a_copy_load(st + 1, v);  // past the end on the last stage; that copy is unused
@@ -295,58 +307,63 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   }
 
   // ------------------------------------------------------------------ epilogue
+  // acc[rb][cb][i] is row 16*rb + 4*(lane/16) + i, column 16*cb + lane%16 of
+  // the wave's 64 columns: position p0 + cb/2, half h = cb%2.
   const bool use0 = p0 < NB, use1 = p0 + 1 < NB;
-  const int n = lane & 31;
+  const int n16 = lane & 15;
+  // FC1 writes the FP32 activation output (NVFP4 path: it is requantized next)
+  // or its BF16 rounding (W4A16: it is FC2's input as it is).
+  auto store_h = [&](long idx, float h) {
+    if constexpr (AK == 1)
+      static_cast<uint16_t*>(P.out)[idx] = (uint16_t)f32_to_bf16(h);
+    else
+      static_cast<float*>(P.out)[idx] = h;
+  };
 #pragma unroll
-  for (int rb = 0; rb < (TWO ? 2 : 1); ++rb) {
-    const floatx16& c0 = rb ? acc10 : acc00;
-    const floatx16& c1 = rb ? acc11 : acc01;
+  for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * rb + 4 * (lane >> 4) + i;
       if (m >= mrows) continue;
       const float s = s_row[m];
       const long orow = (long)(row0 + m) * P.out_stride;
-      // FC1 writes the FP32 activation output (NVFP4 path: it is requantized
-      // next) or its BF16 rounding (W4A16: it is FC2's input as it is).
-      auto store_h = [&](long idx, float h) {
-        if constexpr (AK == 1)
-          static_cast<uint16_t*>(P.out)[idx] = (uint16_t)f32_to_bf16(h);
-        else
-          static_cast<float*>(P.out)[idx] = h;
-      };
-      if constexpr (MODE == kFc1Relu2) {
-        if (use0) {
-          const float y = __builtin_fmaxf(c0[r] * s, 0.0f);
-          store_h(orow + kColBlock * p0 + n, y * y);
-        }
-        if (use1) {
-          const float y = __builtin_fmaxf(c1[r] * s, 0.0f);
-          store_h(orow + kColBlock * (p0 + 1) + n, y * y);
-        }
-      } else if constexpr (MODE == kFc1Swiglu) {
-        // p0 is even: block p0 holds gate rows, p0 + 1 the matching up rows.
-        if (use0) {
-          float g = c0[r] * s;
-          float u = c1[r] * s;
-          if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
-            g = __builtin_fminf(g, P.swiglu_limit);
-            u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float c0 = acc[rb][h][i], c1 = acc[rb][2 + h][i];  // positions p0, p0 + 1
+        const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
+        if constexpr (MODE == kFc1Relu2) {
+          if (use0) {
+            const float y = __builtin_fmaxf(c0 * s, 0.0f);
+            store_h(orow + col0, y * y);
           }
-          const float silu = g / (1.0f + expf(-g));
-          store_h(orow + kColBlock * (p0 >> 1) + n, silu * u);
+          if (use1) {
+            const float y = __builtin_fmaxf(c1 * s, 0.0f);
+            store_h(orow + col1, y * y);
+          }
+        } else if constexpr (MODE == kFc1Swiglu) {
+          // p0 is even: position p0 holds gate rows, p0 + 1 the matching up rows.
+          if (use0) {
+            float g = c0 * s;
+            float u = c1 * s;
+            if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
+              g = __builtin_fminf(g, P.swiglu_limit);
+              u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
+            }
+            const float silu = g / (1.0f + expf(-g));
+            store_h(orow + kColBlock * (p0 >> 1) + 16 * h + n16, silu * u);
+          }
+        } else if constexpr (MODE == kFc2Fused) {
+          // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
+          const int f = P.out_route[row0 + m];
+          const float wgt = P.out_w[f];
+          float* acc_row = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
+          if (use0) unsafeAtomicAdd(acc_row + col0, wgt * (c0 * s));
+          if (use1) unsafeAtomicAdd(acc_row + col1, wgt * (c1 * s));
+        } else {
+          uint16_t* out = static_cast<uint16_t*>(P.out) + orow;
+          if (use0) out[col0] = (uint16_t)f32_to_bf16(c0 * s);
+          if (use1) out[col1] = (uint16_t)f32_to_bf16(c1 * s);
         }
-      } else if constexpr (MODE == kFc2Fused) {
-        // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
-        const int f = P.out_route[row0 + m];
-        const float wgt = P.out_w[f];
-        float* acc = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
-        if (use0) unsafeAtomicAdd(acc + kColBlock * p0 + n, wgt * (c0[r] * s));
-        if (use1) unsafeAtomicAdd(acc + kColBlock * (p0 + 1) + n, wgt * (c1[r] * s));
-      } else {
-        uint16_t* out = static_cast<uint16_t*>(P.out) + orow;
-        if (use0) out[kColBlock * p0 + n] = (uint16_t)f32_to_bf16(c0[r] * s);
-        if (use1) out[kColBlock * (p0 + 1) + n] = (uint16_t)f32_to_bf16(c1[r] * s);
       }
     }
   }
@@ -389,10 +406,12 @@ __global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcPar
     s_row[tid] = P.a_scale ? P.a_scale[ar] * P.w_alpha[e] : P.w_alpha[e];
   }
   __syncthreads();
-  if (mrows > 32)
-    fc_tile<MODE, true, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
-  else
-    fc_tile<MODE, false, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
+  switch ((mrows + 15) >> 4) {  // 16-row blocks that hold rows of this tile
+    case 1: fc_tile<MODE, 1, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 2: fc_tile<MODE, 2, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 3: fc_tile<MODE, 3, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    default: fc_tile<MODE, 4, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+  }
 }
 
 hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s) {

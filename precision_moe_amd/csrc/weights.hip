@@ -93,12 +93,18 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
       }
       sf = quant_block16(x, alpha, lo, hi);
     }
+    // block j of chunk c is half jj of k-step s; its row sits in 16-column
+    // block h of the position. Lane 32*jj + col%16 holds elements 0..7, lane
+    // + 16 elements 8..15, each as word 2h + s of its 16 bytes; the scale is
+    // byte 2h + s of dword col%16 + 16*jj.
     const int c = kb >> 2, j = kb & 3;
+    const int s = j >> 1, jj = j & 1, h = col >> 4, n16 = col & 15;
+    const int lane_lo = 32 * jj + n16;
     const long slab = (tile_base + c) * kColTileBlocks + pos;
     uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + slab * 1024);
-    cdst[col * 4 + j] = lo;         // lane col (elements 0..7 of the block)
-    cdst[(col + 32) * 4 + j] = hi;  // lane col + 32 (elements 8..15)
-    scales[slab * 128 + col * 4 + j] = (uint8_t)sf;
+    cdst[lane_lo * 4 + 2 * h + s] = lo;
+    cdst[(lane_lo + 16) * 4 + 2 * h + s] = hi;
+    scales[slab * 128 + (n16 + 16 * jj) * 4 + 2 * h + s] = (uint8_t)sf;
   }
 }
 

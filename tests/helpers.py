@@ -23,10 +23,12 @@ def canonical_from_prepared(codes, scales, E, N, Kd, gated_I=0, check_padding=Tr
     NB, KC = N // 32, Kd // 64
     NBp = -(-NB // TILE) * TILE
     NT = NBp // TILE
-    c = np.asarray(codes, np.uint8).reshape(E, NT, KC, TILE, 2, 32, 4, 4)  # e ct c pos h col j b
-    c = c.transpose(0, 1, 3, 5, 2, 6, 4, 7).reshape(E, NBp * 32, KC * 32)  # e (ct pos col) (c j h b)
-    s = np.asarray(scales, np.uint8).reshape(E, NT, KC, TILE, 32, 4)       # e ct c pos col j
-    s = s.transpose(0, 1, 3, 4, 2, 5).reshape(E, NBp * 32, KC * 4)
+    # codes: lane = 16*g + n16, bytes (2h + s)*4 + b: element k = 32 s + 8 g + 2 b (+1), row 16 h + n16
+    c = np.asarray(codes, np.uint8).reshape(E, NT, KC, TILE, 4, 16, 2, 2, 4)  # e ct c pos g n16 h s b
+    c = c.transpose(0, 1, 3, 6, 5, 2, 7, 4, 8).reshape(E, NBp * 32, KC * 32)  # e (ct pos h n16) (c s g b)
+    # scales: dword d = n16 + 16 jj, byte 2h + s: block 2s + jj of row 16 h + n16
+    s = np.asarray(scales, np.uint8).reshape(E, NT, KC, TILE, 2, 16, 2, 2)     # e ct c pos jj n16 h s
+    s = s.transpose(0, 1, 3, 6, 5, 2, 7, 4).reshape(E, NBp * 32, KC * 4)       # e (ct pos h n16) (c s jj)
     if check_padding:
         assert not c[:, NB * 32:].any() and not s[:, NB * 32:].any(), "padding blocks must be zero"
     c, s = c[:, :NB * 32], s[:, :NB * 32]

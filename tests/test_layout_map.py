@@ -26,17 +26,21 @@ def test_inverse_layout_map(gated, I):
                 n = rows[p * 32 + col]
                 if gated:
                     assert n == (I if p % 2 else 0) + 32 * (p // 2) + col
-                for c in range(KC):
+            for c in range(KC):
+                slab = ((e * NT + p // TILE) * KC + c) * TILE + p % TILE
+                for lane in range(64):
                     for h in range(2):
-                        for j in range(4):
+                        n = rows[p * 32 + 16 * h + lane % 16]
+                        for s_ in range(2):
                             for i in range(8):
-                                k = c * 64 + 16 * j + 8 * h + i
+                                k = c * 64 + 32 * s_ + 8 * (lane // 16) + i
                                 nib = (canon[e, n, k // 2] >> (4 * (k % 2))) & 15
-                                slab = ((e * NT + p // TILE) * KC + c) * TILE + p % TILE
-                                off = (slab * 64 + col + 32 * h) * 16 + j * 4 + i // 2
+                                off = (slab * 64 + lane) * 16 + (2 * h + s_) * 4 + i // 2
                                 prep[off] |= nib << (4 * (i % 2))
-                    for j in range(4):
-                        slab = ((e * NT + p // TILE) * KC + c) * TILE + p % TILE
-                        prep_s[(slab * 32 + col) * 4 + j] = canon_s[e, n, c * 4 + j]
+                for d in range(32):
+                    for h in range(2):
+                        n = rows[p * 32 + 16 * h + d % 16]
+                        for s_ in range(2):
+                            prep_s[(slab * 32 + d) * 4 + 2 * h + s_] = canon_s[e, n, c * 4 + 2 * s_ + d // 16]
     cq, cs = canonical_from_prepared(prep, prep_s, E, N, H, gI)
     assert np.array_equal(cq, canon) and np.array_equal(cs, canon_s)
