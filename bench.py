@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the per-token NVFP4 routed-MoE hot path on one MI355X.
 
-One step = pmoe_quantize_input_per_token + pmoe_routed_moe (routing, FC1 +
-activation, requantization, FC2, fixed-order finalize) over one batch of
+One step = pmoe_moe_forward on BF16 activations (per-token quantization
+overlapped with the routing, FC1 + activation, requantization, FC2,
+fixed-order finalize) over one batch of
 synthetic tokens already resident in HBM, with weights prepared beforehand
 (preparation is timed separately and reported as `prepare`).
 
@@ -157,6 +158,9 @@ def main():
     out = torch.empty((T, w.H), dtype=torch.bfloat16, device=dev)
 
     def step():
+        pm.moe_forward(x, ids, wts, P, workspace=ws, out=out)
+
+    def step_separate_quantize():
         pm.quantize_input_per_token(x, out=(xq, xs, xg))
         pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out)
 
@@ -227,12 +231,10 @@ def main():
         pm.routed_moe_w4a16(x, ids, wts, P, workspace=ws, out=out)
 
     def step_one_stream():
-        pm.quantize_input_per_token(x, out=(xq, xs, xg))
-        pm.routed_moe_ex(xq, xs, xg, ids, wts, P, streams=1, workspace=ws, out=out)
+        pm.moe_forward(x, ids, wts, P, streams=1, workspace=ws, out=out)
 
     def step_fused():
-        pm.quantize_input_per_token(x, out=(xq, xs, xg))
-        pm.routed_moe_ex(xq, xs, xg, ids, wts, P, finalize="fused", workspace=ws, out=out)
+        pm.moe_forward(x, ids, wts, P, finalize="fused", workspace=ws, out=out)
 
     logits = torch.from_numpy(synth.router_logits(w)).to(dev)
     r_ids = torch.empty_like(ids)
@@ -244,7 +246,9 @@ def main():
     recipes = {}
     flops_step = 2.0 * R_rows * (w.N1 * w.H + w.H * w.I)
     for name, fn in (("per_tensor", step_per_tensor), ("weight_only_w4a16", step_w4a16),
-                     ("per_token_ordered_finalize", step), ("per_token_one_stream", step_one_stream),
+                     ("per_token_ordered_finalize", step),
+                     ("per_token_separate_quantize", step_separate_quantize),
+                     ("per_token_one_stream", step_one_stream),
                      ("per_token_fused_finalize", step_fused),
                      ("router_topk", step_router)):
         for _ in range(max(args.warmup // 2, 2)):

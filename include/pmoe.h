@@ -331,6 +331,8 @@ typedef struct pmoe_moe_options {
   int streams;            /* 0: automatic; 1: one stream; 2: the two halves of the experts
                              run FC1 -> requant -> FC2 on the caller's stream and on a second
                              stream, joined before the finalize (same bits either way)   */
+  const float* a1_scale;  /* pmoe_moe_forward, per-tensor recipe: device float32 scalar
+                             (the static FC1 input scale); otherwise NULL               */
 } pmoe_moe_options;
 
 /*
@@ -360,6 +362,23 @@ int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float* x_scale,
                        const void* w2_codes, const void* w2_scales, const float* w2_alpha,
                        int act, const pmoe_moe_options* options,
                        void* ws, size_t ws_bytes, void* out, void* stream);
+
+/*
+ * The whole routed layer from BF16 activations: for the NVFP4 recipes the
+ * input is quantized inside the call (per token, or with options->a1_scale for
+ * the per-tensor recipe) on the library's second stream while the routing runs
+ * on the caller's stream, into the workspace; then the path of
+ * pmoe_routed_moe_ex. For PMOE_RECIPE_W4A16 it is pmoe_routed_moe_ex on x.
+ *   x : BF16 [T, H]. Other arguments, options and errors as pmoe_routed_moe_ex
+ *   (options == NULL: per-token, ordered, no clamp). The bits of the result
+ *   equal quantize + pmoe_routed_moe(_ex) on the same inputs.
+ */
+int pmoe_moe_forward(const void* x, const void* topk_ids, int ids_type, const float* topk_w,
+                     int T, int K, int E, int H, int I, int N1, int expert_offset,
+                     const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                     const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                     int act, const pmoe_moe_options* options,
+                     void* ws, size_t ws_bytes, void* out, void* stream);
 
 /*
  * Router front: top-k experts and their routing weights from FP32 logits

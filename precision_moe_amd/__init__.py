@@ -32,7 +32,7 @@ class MoeOptions(ctypes.Structure):
     """pmoe_moe_options (include/pmoe.h)."""
     _fields_ = [("recipe", ctypes.c_int), ("finalize", ctypes.c_int),
                 ("swiglu_limit", ctypes.c_float), ("a2_scale", ctypes.c_void_p),
-                ("streams", ctypes.c_int)]
+                ("streams", ctypes.c_int), ("a1_scale", ctypes.c_void_p)]
 _SIGNATURES = {
     "pmoe_version": (_i, []),
     "pmoe_last_error": (ctypes.c_char_p, []),
@@ -60,6 +60,8 @@ _SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _i, ctypes.POINTER(MoeOptions), _vp,
                                 ctypes.c_size_t, _vp, _vp]),
     "pmoe_router_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "pmoe_moe_forward": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _i, ctypes.POINTER(MoeOptions), _vp, ctypes.c_size_t, _vp, _vp]),
 }
 STEP_ROUTE, STEP_FC1, STEP_REQUANT, STEP_FC2, STEP_FINALIZE = range(5)
 
@@ -381,6 +383,28 @@ def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, 
         W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
         _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, ctypes.byref(opt),
         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_forward(x, topk_ids, topk_w, weights: PreparedWeights, recipe="per_token",
+                finalize="ordered", swiglu_limit=0.0, a1=None, a2=None, act=None, expert_offset=0,
+                workspace=None, out=None, stream=None, streams=0):
+    """The whole routed layer from BF16 activations x [T, H] (pmoe_moe_forward): the NVFP4
+    recipes quantize x inside the call, overlapped with the routing."""
+    T, K = topk_ids.shape
+    W = weights
+    act = W.act if act is None else act
+    x = _bf16_storage(x.contiguous())
+    topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
+    workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
+    opt = MoeOptions(_RECIPES[recipe], _FINALIZE[finalize], float(swiglu_limit),
+                     _f32_scalar(a2).data_ptr() if a2 is not None else None, int(streams),
+                     _f32_scalar(a1).data_ptr() if a1 is not None else None)
+    _check(lib().pmoe_moe_forward(
+        _ptr(x), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1, expert_offset,
+        _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes), _ptr(W.w2_scales),
+        _ptr(W.w2_alpha), act, ctypes.byref(opt), _ptr(workspace), workspace.numel(), _ptr(out),
+        _stream(stream)))
     return out
 
 

@@ -115,7 +115,7 @@ size_t prepare_ws(int E, int N1, int H, int I) {
 // routed_moe workspace layout
 struct MoeLayout {
   size_t off[PMOE_WS_NUM_FIELDS];
-  size_t rank_local, block_counts, tiles, acc32;
+  size_t rank_local, block_counts, tiles, acc32, xq, x_sf, x_scale;
   size_t total;
   int max_tiles;
 };
@@ -143,6 +143,9 @@ MoeLayout moe_layout(int T, int K, int E, int H, int I) {
   L.block_counts = take((size_t)route_blocks((int)TK) * E * 4);
   L.tiles = take((size_t)L.max_tiles * 4 * 4);
   L.acc32 = take((size_t)T * H * 4);
+  L.xq = take((size_t)T * H / 2);
+  L.x_sf = take((size_t)T * H / 16);
+  L.x_scale = take((size_t)T * 4);
   L.total = o;
   return L;
 }
@@ -349,7 +352,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
              const void* w1_scales, const float* w1_alpha, const void* w2_codes,
              const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
              void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f,
-             int streams = 0) {
+             int streams = 0, bool bf16_input = false, const float* a1 = nullptr) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
   if (!(swiglu_limit >= 0.0f)) return fail(PMOE_ERR_ARG, "swiglu_limit must be >= 0");
@@ -362,13 +365,16 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     return fail(PMOE_ERR_ARG, "ids_type must be PMOE_IDS_INT32 or PMOE_IDS_INT64");
   if (T == 0) return ok();
   PMOE_TRY(check_device());
-  if (rc == kW4A16) {
+  if (bf16_input && (first != PMOE_STEP_ROUTE || last != PMOE_STEP_FINALIZE))
+    return fail(PMOE_ERR_ARG, "BF16 input runs the whole path");
+  if (rc == kW4A16 || bf16_input) {
     PMOE_TRY(check_ptr(x, 16, "x"));
   } else {
     PMOE_TRY(check_ptr(x, 16, "xq"));
     PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
   }
-  if (rc == kPerToken) PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  if (rc == kPerToken && !bf16_input) PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
+  if (rc == kPerTensor && bf16_input) PMOE_TRY(check_ptr(a1, 4, "a1_scale"));
   if (rc == kPerTensor) PMOE_TRY(check_ptr(a2, 4, "a2_scale"));
   PMOE_TRY(check_ptr(topk_ids, ids_type == PMOE_IDS_INT64 ? 8 : 4, "topk_ids"));
   PMOE_TRY(check_ptr(topk_w, 4, "topk_w"));
@@ -396,8 +402,27 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   rb.row_of_route = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROW_OF_ROUTE]);
   rb.route_of_row = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROUTE_OF_ROW]);
   auto run = [&](int step) { return first <= step && step <= last; };
-  if (run(PMOE_STEP_ROUTE))
+  if (bf16_input && rc != kW4A16) {
+    // quantize the BF16 activations on the second stream while routing runs
+    // on the caller's; both are joined before FC1
+    uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
+    uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
+    float* wsc = reinterpret_cast<float*>(base + L.x_scale);
+    Aux* aux = nullptr;
+    PMOE_TRY(aux_for_current_device(&aux));
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    PMOE_HIP(hipEventRecord(aux->fork, s));
+    PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
+    PMOE_HIP(launch_quantize_bf16(x, T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, aux->s2));
     PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+    PMOE_HIP(hipEventRecord(aux->join, aux->s2));
+    PMOE_HIP(hipStreamWaitEvent(s, aux->join, 0));
+    x = wq;
+    x_sf = wsf;
+    x_scale = rc == kPerToken ? wsc : nullptr;
+  } else if (run(PMOE_STEP_ROUTE)) {
+    PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+  }
 
   void* h = base + L.off[PMOE_WS_H];  // FP32 h, or BF16 h under W4A16
   uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.off[PMOE_WS_HQ]);
@@ -541,7 +566,7 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
                                    const void* w2_scales, const float* w2_alpha, int act,
                                    const pmoe_moe_options* options, void* ws, size_t ws_bytes,
                                    void* out, void* stream) {
-  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0};
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr};
   if (options) o = *options;
   if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
       o.recipe != PMOE_RECIPE_W4A16)
@@ -553,12 +578,39 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
   if (o.recipe != PMOE_RECIPE_PER_TENSOR && o.a2_scale)
     return fail(PMOE_ERR_ARG, "a2_scale belongs to the per-tensor recipe");
   if (o.streams < 0 || o.streams > 2) return fail(PMOE_ERR_ARG, "streams must be 0, 1 or 2");
+  if (o.a1_scale) return fail(PMOE_ERR_ARG, "a1_scale belongs to pmoe_moe_forward");
   const Recipe rc = static_cast<Recipe>(o.recipe);
   return moe_path(rc, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, x_sf,
                   rc == kPerToken ? x_scale : nullptr, o.a2_scale, topk_ids, ids_type, topk_w, T, K,
                   E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha, w2_codes, w2_scales,
                   w2_alpha, act, ws, ws_bytes, out, stream, o.finalize == PMOE_FINALIZE_FUSED,
                   o.swiglu_limit, o.streams);
+}
+
+PMOE_EXPORT int pmoe_moe_forward(const void* x, const void* topk_ids, int ids_type,
+                                 const float* topk_w, int T, int K, int E, int H, int I, int N1,
+                                 int expert_offset, const void* w1_codes, const void* w1_scales,
+                                 const float* w1_alpha, const void* w2_codes,
+                                 const void* w2_scales, const float* w2_alpha, int act,
+                                 const pmoe_moe_options* options, void* ws, size_t ws_bytes,
+                                 void* out, void* stream) {
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr};
+  if (options) o = *options;
+  if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
+      o.recipe != PMOE_RECIPE_W4A16)
+    return fail(PMOE_ERR_ARG, "unknown recipe");
+  if (o.finalize != PMOE_FINALIZE_ORDERED && o.finalize != PMOE_FINALIZE_FUSED)
+    return fail(PMOE_ERR_ARG, "unknown finalize mode");
+  if (o.swiglu_limit != 0.0f && act != PMOE_ACT_SWIGLU)
+    return fail(PMOE_ERR_ARG, "swiglu_limit needs the SwiGLU activation");
+  if (o.recipe != PMOE_RECIPE_PER_TENSOR && (o.a1_scale || o.a2_scale))
+    return fail(PMOE_ERR_ARG, "a1_scale and a2_scale belong to the per-tensor recipe");
+  if (o.streams < 0 || o.streams > 2) return fail(PMOE_ERR_ARG, "streams must be 0, 1 or 2");
+  const Recipe rc = static_cast<Recipe>(o.recipe);
+  return moe_path(rc, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, nullptr, nullptr, o.a2_scale, topk_ids,
+                  ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha,
+                  w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream,
+                  o.finalize == PMOE_FINALIZE_FUSED, o.swiglu_limit, o.streams, true, o.a1_scale);
 }
 
 PMOE_EXPORT int pmoe_router_topk(const float* logits, int T, int E, int K, int renormalize,

@@ -145,11 +145,103 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
   route_of_row[row] = f;
 }
 
+// The whole routing in one workgroup of 1024 threads, for up to
+// kRouteSmall routes (one launch instead of three). Counts come from integer
+// LDS atomics (order-free), then the routes are walked in chunks of 1024 in
+// route order: a route's row is its expert's start + the rows its expert got
+// in earlier chunks + in earlier waves of this chunk + its rank among the
+// wave's lanes with the same expert (ballots on the expert id bits), which is
+// the same stable order as the three-kernel path.
+constexpr int kRouteSmall = 8192;
+
+template <typename IdT>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
+    int* __restrict__ expert_offsets, int* __restrict__ tiles, int* __restrict__ counters,
+    int* __restrict__ row_of_route, int* __restrict__ route_of_row) {
+  __shared__ int base[kMaxExperts];      // counts, then each expert's next free row
+  __shared__ int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk (kept at 0)
+  __shared__ int sh[1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kMaxExperts; i += 1024) base[i] = 0;
+  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int f = tid; f < TK; f += 1024) {
+    const int e = local_expert(ids, f, E, offset);
+    if (e >= 0) atomicAdd(&base[e], 1);
+  }
+  __syncthreads();
+  const int total = tid < E ? base[tid] : 0;
+  const int incl = block_inclusive_scan_1024(total, sh);
+  const int start = incl - total;
+  const int R = sh[1023];
+  __syncthreads();
+  const int ntiles = (total + kTileM - 1) / kTileM;
+  const int tincl = block_inclusive_scan_1024(ntiles, sh);
+  const int tstart = tincl - ntiles;
+  const int T_tiles = sh[1023];
+  if (tid < E) {
+    expert_offsets[tid] = start;
+    base[tid] = start;
+    for (int i = 0; i < ntiles; ++i)
+      reinterpret_cast<int4*>(tiles)[tstart + i] = make_int4(tid, i * kTileM, tstart, ntiles);
+  }
+  if (tid == 0) {
+    expert_offsets[E] = R;
+    counters[0] = R;
+    counters[1] = T_tiles;
+  }
+  if (tid == (E + 1) / 2) {  // the first expert of the second half (E itself when E == 1)
+    counters[2] = tstart;
+    counters[3] = start;
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < TK; c0 += 1024) {
+    const int f = c0 + tid;
+    const int e = f < TK ? local_expert(ids, f, E, offset) : -1;
+    uint64_t match = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(bit);
+      match &= bit ? set : ~set;
+    }
+    const int rank_w = __popcll(match & below);
+    if (e >= 0 && rank_w == 0) wcnt[wave][e] = __popcll(match);
+    __syncthreads();
+    if (e >= 0) {
+      int row = base[e] + rank_w;
+      for (int w = 0; w < wave; ++w) row += wcnt[w][e];
+      row_of_route[f] = row;
+      route_of_row[row] = f;
+    } else if (f < TK) {
+      row_of_route[f] = -1;
+    }
+    __syncthreads();
+    if (e >= 0 && rank_w == 0) {
+      atomicAdd(&base[e], __popcll(match));
+      wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_offset,
                         const RouteBuffers& b, hipStream_t s) {
   const int NB = route_blocks(TK);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (TK <= kRouteSmall) {
+    if (ids64)
+      route_small_kernel<long long><<<1, 1024, 0, s>>>(
+          static_cast<const long long*>(ids), TK, E, expert_offset, nbits, b.expert_offsets, b.tiles,
+          b.counters, b.row_of_route, b.route_of_row);
+    else
+      route_small_kernel<int><<<1, 1024, 0, s>>>(
+          static_cast<const int*>(ids), TK, E, expert_offset, nbits, b.expert_offsets, b.tiles,
+          b.counters, b.row_of_route, b.route_of_row);
+    return hipGetLastError();
+  }
   if (ids64)
     route_count_kernel<long long><<<NB, 256, 0, s>>>(static_cast<const long long*>(ids), TK, E,
                                                      expert_offset, nbits, b.rank_local,

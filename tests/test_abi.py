@@ -135,6 +135,17 @@ def test_options_and_router_validation():
     z[6] = 0                                    # T == 0: no-op with any valid options
     assert lib.pmoe_routed_moe_ex(*z, ctypes.byref(pm.MoeOptions(2, 1, 5.0, None)), *tail) == 0
     assert lib.pmoe_routed_moe_ex(*z, None, *tail) == 0
+    a1 = ctypes.c_float(1.0)
+    o = pm.MoeOptions(0, 0, 0.0, None, 0, ctypes.addressof(a1))
+    assert lib.pmoe_routed_moe_ex(*base, ctypes.byref(o), *tail) == 7    # a1 is forward's
+    fwd = base[:1] + base[3:]                   # forward: x, ids, ... (no x_sf / x_scale)
+    assert lib.pmoe_moe_forward(*fwd, ctypes.byref(o), *tail) == 7      # a1 with per-token
+    assert lib.pmoe_moe_forward(*fwd, ctypes.byref(pm.MoeOptions(3, 0, 0.0, None)), *tail) == 7
+    zf = list(fwd)
+    zf[4] = 0                                   # T == 0
+    assert lib.pmoe_moe_forward(*zf, None, *tail) == 0
+    o = pm.MoeOptions(1, 0, 0.0, None, 0, ctypes.addressof(a1))
+    assert lib.pmoe_moe_forward(*zf, ctypes.byref(o), *tail) == 0
     assert lib.pmoe_router_topk(None, 0, 64, 6, 0, None, None, None) == 0
     assert lib.pmoe_router_topk(None, 4, 64, 0, 0, None, None, None) == 3
     assert lib.pmoe_router_topk(None, 4, 4, 6, 0, None, None, None) == 3

@@ -171,11 +171,17 @@ def _route_case(name, rng):
         return rng.integers(0, 1024, (700, 8)), 1024, 0
     if name == "single":
         return np.array([[5, 1]]), 6, 0
+    if name == "one_launch_limit":        # 8192 routes: the largest one-workgroup routing
+        ids = rng.integers(0, 64, (1024, 8))
+        ids[::7, 3] = -1
+        return ids, 64, 0
+    if name == "past_one_launch":         # 8200 routes: the three-kernel routing
+        return rng.integers(0, 64, (1025, 8)), 64, 0
     raise KeyError(name)
 
 
 @pytest.mark.parametrize("case", ["random", "one_expert", "invalid_and_offset", "skewed_large",
-                                  "many_experts", "single"])
+                                  "many_experts", "single", "one_launch_limit", "past_one_launch"])
 @pytest.mark.parametrize("ids_dtype", [np.int32, np.int64])
 def test_routing_matches_oracle(pm, case, ids_dtype):
     """Row maps and expert offsets of routed_moe's workspace equal the oracle's stable routing."""

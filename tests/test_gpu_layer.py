@@ -229,3 +229,51 @@ def test_edges_single_token_and_router_k_equals_e(pm):
     assert np.array_equal(rid.cpu().numpy(), oid)
     np.testing.assert_allclose(rw.cpu().numpy(), ow, rtol=1e-5)
     np.testing.assert_allclose(rw.cpu().numpy().sum(axis=1), 1.0, rtol=1e-5)
+
+
+# ----------------------------------------------------------------------------- BF16 forward
+@pytest.mark.parametrize("name,recipe,finalize", [
+    ("tiny", "per_token", "ordered"), ("swiglu", "per_tensor", "ordered"),
+    ("swiglu", "w4a16", "ordered"), ("relu2", "per_token", "fused"),
+    ("ep4_t1024", "per_token", "ordered"), ("ep4_t512", "per_tensor", "ordered")])
+def test_forward_equals_quantize_then_path(pm, name, recipe, finalize):
+    """pmoe_moe_forward (quantize overlapped with routing) gives the bits of the
+    separate quantize call followed by pmoe_routed_moe_ex; ordered finalize
+    bit for bit, the fused one to its tolerance."""
+    import torch
+    w = synth.WORKLOADS[name]
+    x = synth.activations(w)
+    ids, wts = (dev(a) for a in synth.router(w))
+    xd = dev_bf16(x)
+    a1 = torch.tensor([float(2688.0 / np.abs(bf16_to_f32(x)).max())], device="cuda")
+    a2 = torch.tensor([2688.0 / 0.5], dtype=torch.float32, device="cuda")
+    scales = (a1, a2) if recipe == "per_tensor" else None
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"), input_scales=scales)
+    kw = dict(recipe=recipe, finalize=finalize, a2=a2 if recipe == "per_tensor" else None)
+    if recipe == "per_token":
+        xin = pm.quantize_input_per_token(xd)
+    elif recipe == "per_tensor":
+        xin = pm.quantize_input_per_tensor(xd, a1) + (None,)
+    else:
+        xin = (xd, None, None)
+    ref = pm.routed_moe_ex(*xin, ids, wts, P, **kw)
+    outs = [pm.moe_forward(xd, ids, wts, P, a1=a1 if recipe == "per_tensor" else None,
+                           streams=s, **kw) for s in (0, 1, 2)]
+    _sync()
+    for got in outs:
+        if finalize == "ordered":
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+        else:
+            _assert_rows_close(bf16_bits(got), bf16_bits(ref), "forward (fused)")
+    del P
+    torch.cuda.empty_cache()
+
+
+def test_forward_matches_oracle(pm):
+    w = synth.WORKLOADS["swiglu"]
+    x = synth.activations(w)
+    ids, wts = synth.router(w)
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    got = pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P)
+    _sync()
+    _assert_rows_close(bf16_bits(got), _oracle(w, x, ids, wts).out, "forward")
