@@ -4,10 +4,11 @@
 // contract, 'Compute order'].
 //
 // Work unit: one M-tile (up to 64 expert-sorted rows of one expert, from the
-// device tile list) x one column tile (8 prepared column blocks = 256 weight
-// rows). A workgroup is 4 waves; wave w owns column blocks 2w and 2w+1 and all
-// rows of the tile, as 2 x 2 accumulators of v_mfma_f32_32x32x16_f16. A tile
-// with at most 32 rows skips the upper row block entirely.
+// device tile list) x one column tile (8 prepared positions of 32 weight rows
+// = 256 columns). A workgroup is 4 waves; wave w owns positions 2w and 2w+1
+// (four 16-column blocks) and every 16-row block of the tile that holds rows,
+// as NRB x 4 accumulators of v_mfma_f32_16x16x32_f16 (NRB = 1..4: a ragged
+// tile neither stages nor multiplies the row blocks past its last row).
 //
 // Reduction loop, in stages of 128 elements (two 64-element chunks):
 //   * A (activations, NVFP4 rows gathered by route for FC1, contiguous rows
@@ -15,16 +16,18 @@
 //     their two block scales of one row, decodes them exactly to FP16 and writes
 //     them into a multi-buffered LDS stage [64 rows][128 k]. Within a row the
 //     16-byte slots are XOR-swizzled by the row index, so both the stage
-//     writes and the MFMA fragment reads hit 8 distinct bank groups per 8
-//     lanes (conflict-free).
+//     writes and the MFMA fragment reads hit distinct bank groups (conflict
+//     free). BF16 rows (W4A16) are copied into the stage as they are.
 //   * B (weights, prepared layout): a column tile's chunk is one contiguous
 //     9 KB slab, so a workgroup streams a single sequential region; per chunk
-//     and column block each lane loads one 16-byte span (1 KB per wave-load)
-//     and one dword of four E4M3 scales, by buffer loads with scalar chunk
+//     and position each lane loads one 16-byte span (1 KB per wave-load) and
+//     one dword of four E4M3 scales, by buffer loads with scalar chunk
 //     offsets. Loads run kRing - 1 chunks ahead in a register ring; decoding
-//     happens in registers straight into MFMA operand order, and every
-//     decoded B fragment feeds both row blocks.
-//   * The MFMA k-step of 16 is exactly one NVFP4 block; FP32 accumulation.
+//     happens in registers straight into MFMA operand order (each block scale
+//     multiplied into its 16 decoded values, exact in FP16), and every decoded
+//     B fragment feeds all row blocks.
+//   * One MFMA k-step of 32 spans two NVFP4 blocks of both operands, whose
+//     scales are already in the decoded values; FP32 accumulation.
 // Epilogue: y = acc * fp32(g_row * alpha_e) (scales applied after
 // accumulation, never folded into decoded values), then
 //   FC1 squared ReLU: h = max(y, 0)^2;  FC1 SwiGLU: h = silu(gate) * up (gate
@@ -370,11 +373,8 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
 }
 
 template <int MODE, int AK>
-__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcParams P) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
-  __shared__ int a_row[kTileM];
-  __shared__ float s_row[kTileM];
-
+__device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
+                                         int* a_row, float* s_row) {
   const int tid = threadIdx.x;
   // Work item -> (tile, column tile): items are numbered expert-major, then
   // column tile, then M-tile; XCD x = blockIdx % 8 takes items
@@ -414,24 +414,50 @@ __global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcPar
   }
 }
 
+// One launch over the tiles of every local expert.
+template <int MODE, int AK>
+__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
+  __shared__ int a_row[kTileM];
+  __shared__ float s_row[kTileM];
+  fc_block<MODE, AK>(P, a_lds, a_row, s_row);
+}
+
+// The same code over one half of the experts (P.part = 1 or 2); a kernel of
+// its own name so that a trace tells the half launches from the whole ones.
+template <int MODE, int AK>
+__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_half_kernel(FcParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
+  __shared__ int a_row[kTileM];
+  __shared__ float s_row[kTileM];
+  fc_block<MODE, AK>(P, a_lds, a_row, s_row);
+}
+
+template <int MODE, int AK>
+void launch_fc_mode(const FcParams& p, long grid, hipStream_t s) {
+  if (p.part)
+    fc_half_kernel<MODE, AK><<<grid, kThreads, 0, s>>>(p);
+  else
+    fc_kernel<MODE, AK><<<grid, kThreads, 0, s>>>(p);
+}
+
+template <int AK>
+void launch_fc_ak(FcMode mode, const FcParams& p, long grid, hipStream_t s) {
+  switch (mode) {
+    case kFc1Relu2: launch_fc_mode<kFc1Relu2, AK>(p, grid, s); break;
+    case kFc1Swiglu: launch_fc_mode<kFc1Swiglu, AK>(p, grid, s); break;
+    case kFc2: launch_fc_mode<kFc2, AK>(p, grid, s); break;
+    case kFc2Fused: launch_fc_mode<kFc2Fused, AK>(p, grid, s); break;
+  }
+}
+
 hipError_t launch_fc(FcMode mode, const FcParams& p, hipStream_t s) {
   const long blocks = (long)p.max_tiles * fc_col_tiles(p.NB);
   const long grid = (blocks + 7) / 8 * 8;
-  if (p.a_bf16) {
-    switch (mode) {
-      case kFc1Relu2: fc_kernel<kFc1Relu2, 1><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc1Swiglu: fc_kernel<kFc1Swiglu, 1><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc2: fc_kernel<kFc2, 1><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc2Fused: fc_kernel<kFc2Fused, 1><<<grid, kThreads, 0, s>>>(p); break;
-    }
-  } else {
-    switch (mode) {
-      case kFc1Relu2: fc_kernel<kFc1Relu2, 0><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc1Swiglu: fc_kernel<kFc1Swiglu, 0><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc2: fc_kernel<kFc2, 0><<<grid, kThreads, 0, s>>>(p); break;
-      case kFc2Fused: fc_kernel<kFc2Fused, 0><<<grid, kThreads, 0, s>>>(p); break;
-    }
-  }
+  if (p.a_bf16)
+    launch_fc_ak<1>(mode, p, grid, s);
+  else
+    launch_fc_ak<0>(mode, p, grid, s);
   return hipGetLastError();
 }
 

@@ -146,13 +146,17 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
 }
 
 // The whole routing in one workgroup of 1024 threads, for up to
-// kRouteSmall routes (one launch instead of three). Counts come from integer
-// LDS atomics (order-free), then the routes are walked in chunks of 1024 in
-// route order: a route's row is its expert's start + the rows its expert got
-// in earlier chunks + in earlier waves of this chunk + its rank among the
-// wave's lanes with the same expert (ballots on the expert id bits), which is
-// the same stable order as the three-kernel path.
+// kRouteSmall routes (one launch instead of three). Each thread loads all of
+// its ids up front (one memory latency, not one per chunk). Routes are taken
+// in chunks of 1024 in route order; within a wave, lanes with the same expert
+// find each other by ballots on the expert id bits, which gives each route its
+// rank among them and one leader per (wave, expert) that adds the group's size
+// to the expert's count (few LDS atomics even on a hot expert). A route's row
+// is then its expert's start + the rows its expert got in earlier chunks + in
+// earlier waves of this chunk + its rank: the same stable order as the
+// three-kernel path.
 constexpr int kRouteSmall = 8192;
+constexpr int kRouteSmallPer = kRouteSmall / 1024;
 
 template <typename IdT>
 __global__ __launch_bounds__(1024) void route_small_kernel(
@@ -163,12 +167,28 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   __shared__ int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk (kept at 0)
   __shared__ int sh[1024];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ev[kRouteSmallPer], rank[kRouteSmallPer], cnt[kRouteSmallPer];
+#pragma unroll
+  for (int i = 0; i < kRouteSmallPer; ++i) {
+    const int f = i * 1024 + tid;
+    ev[i] = f < TK ? local_expert(ids, f, E, offset) : -1;
+  }
   for (int i = tid; i < kMaxExperts; i += 1024) base[i] = 0;
   for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  for (int f = tid; f < TK; f += 1024) {
-    const int e = local_expert(ids, f, E, offset);
-    if (e >= 0) atomicAdd(&base[e], 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < kRouteSmallPer; ++i) {
+    const int e = ev[i];
+    uint64_t match = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(bit);
+      match &= bit ? set : ~set;
+    }
+    rank[i] = __popcll(match & below);
+    cnt[i] = __popcll(match);
+    if (e >= 0 && rank[i] == 0) atomicAdd(&base[e], cnt[i]);
   }
   __syncthreads();
   const int total = tid < E ? base[tid] : 0;
@@ -195,22 +215,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     counters[2] = tstart;
     counters[3] = start;
   }
-  __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < TK; c0 += 1024) {
-    const int f = c0 + tid;
-    const int e = f < TK ? local_expert(ids, f, E, offset) : -1;
-    uint64_t match = __ballot(e >= 0);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t set = __ballot(bit);
-      match &= bit ? set : ~set;
-    }
-    const int rank_w = __popcll(match & below);
-    if (e >= 0 && rank_w == 0) wcnt[wave][e] = __popcll(match);
-    __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRouteSmallPer; ++i) {
+    if (i * 1024 >= TK) break;  // uniform across the workgroup
+    const int f = i * 1024 + tid;
+    const int e = ev[i];
+    const bool lead = e >= 0 && rank[i] == 0;
+    if (lead) wcnt[wave][e] = cnt[i];
+    __syncthreads();  // (also orders the first chunk after base = start)
     if (e >= 0) {
-      int row = base[e] + rank_w;
+      int row = base[e] + rank[i];
       for (int w = 0; w < wave; ++w) row += wcnt[w][e];
       row_of_route[f] = row;
       route_of_row[row] = f;
@@ -218,8 +232,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
       row_of_route[f] = -1;
     }
     __syncthreads();
-    if (e >= 0 && rank_w == 0) {
-      atomicAdd(&base[e], __popcll(match));
+    if (lead) {
+      atomicAdd(&base[e], cnt[i]);
       wcnt[wave][e] = 0;
     }
     __syncthreads();

@@ -1,8 +1,10 @@
 """Summaries of rocprofv3 output for the pmoe kernels (short text files).
 
     python -m precision_moe_amd.profiling stats <rocprofv3 csv dir> <workload> <out.txt> "<command>"
+        [<kernel> <n>]
         per-kernel call count and average / total duration from a
-        `rocprofv3 --kernel-trace --stats --output-format csv` run
+        `rocprofv3 --kernel-trace --stats --output-format csv` run; with a
+        kernel name and n, also the average of that kernel's first n dispatches
     python -m precision_moe_amd.profiling traffic <fetch dir> <write dir> <copy fetch dir>
         <copy write dir> <copy bytes> <kernel substring> <workload> <out.txt> "<commands>"
         HBM bytes per dispatch of one kernel from `--pmc FETCH_SIZE` and
@@ -25,6 +27,10 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gemm.hip", "device.h", "kernels.h")]
+
+
+# FLOPs of one v_mfma_f32_16x16x32_f16 / _bf16 wave instruction (the grouped GEMMs' only MFMA)
+MFMA_FLOPS = 2 * 16 * 16 * 32
 
 
 def _code_only(text):
@@ -94,7 +100,7 @@ def counter_means(directory, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def write_stats(directory, workload, out, command):
+def write_stats(directory, workload, out, command, first=None):
     st = kernel_stats(directory)
     lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}",
              "# kernel | calls | avg us | total us"]
@@ -104,8 +110,22 @@ def write_stats(directory, workload, out, command):
     other = [v for k, v in st.items() if "pmoe" not in k]
     lines.append(f"(other kernels: input generation and setup) | {sum(c for c, _, _ in other)} | - | "
                  f"{sum(t for _, _, t in other):.1f}")
+    if first:
+        kernel, n = first
+        durs = first_dispatches(directory, kernel, n)
+        lines.append(f"# {kernel}, its first {len(durs)} dispatches in launch order (bench.py's "
+                     f"FC1 loop, timed there with HIP events): avg us "
+                     f"{sum(durs) / max(len(durs), 1):.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def first_dispatches(directory, kernel, n):
+    """Durations (us) of the first n dispatches of `kernel` (exact short name) by start time."""
+    rows = [r for r in _rows(directory, "*kernel_trace.csv")
+            if _short(_col(r, "Kernel_Name")) == kernel]
+    rows.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
+    return [(int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3 for r in rows[:n]]
 
 
 def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, workload, out, command):
@@ -165,7 +185,7 @@ def write_table(kt_dir, fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, mfma_d
         f"# HBM bytes = FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {wf:.4f} (factors from a {copy_bytes}-byte "
         "device copy); GB/s over the kernel trace's average duration",
         "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (duration x 2.4 GHz x 1024 SIMDs): the share of the "
-        "nominal MFMA issue capacity; MFMA TFLOP/s = SQ_INSTS_MFMA x 32768 (32x32x16) / duration, "
+        "nominal MFMA issue capacity; MFMA TFLOP/s = SQ_INSTS_MFMA x 16384 (16x16x32) / duration, "
         "padded rows included",
         "# kernel | avg us | read MB | write MB | HBM GB/s | MFMA insts | MFMA busy | MFMA TFLOP/s",
     ]
@@ -175,7 +195,7 @@ def write_table(kt_dir, fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, mfma_d
         rd = fetch[k] * 1024 * ff
         wr = write.get(k, 0.0) * 1024 * wf
         util = busy.get(k, 0.0) / (avg * 1e-6 * 2.4e9 * 1024)
-        tf = insts.get(k, 0.0) * 32768 / (avg * 1e-6) / 1e12
+        tf = insts.get(k, 0.0) * MFMA_FLOPS / (avg * 1e-6) / 1e12
         lines.append(f"{k} | {avg:.2f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / (avg * 1e3):.0f} | "
                      f"{insts.get(k, 0.0):.4g} | {util:.3f} | {tf:.0f}")
     with open(out, "w") as f:
@@ -200,7 +220,8 @@ def read_traffic(path, workload):
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "stats":
-        write_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+        first = (sys.argv[6], int(sys.argv[7])) if len(sys.argv) > 7 else None
+        write_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], first)
     elif cmd == "traffic":
         write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7],
                       sys.argv[8], sys.argv[9], sys.argv[10])

@@ -1,5 +1,7 @@
 """Pins of the oracle's MoE pipeline: gating, routing, exact GEMM sums, finalize order,
 brute-force MoE agreement and plausibility against the unquantized MoE."""
+import zlib
+
 import numpy as np
 import pytest
 
@@ -42,7 +44,7 @@ def _route_brute(ids, E, off):
 
 @pytest.mark.parametrize("case", ["random", "one_expert", "empty_experts", "invalid", "offset", "int64"])
 def test_routing_brute_force(case):
-    rng = np.random.default_rng(hash(case) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
     T, K, E, off = 37, 4, 8, 0
     ids = rng.integers(0, E, (T, K))
     if case == "one_expert":
