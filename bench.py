@@ -15,7 +15,9 @@ Prints one JSON line. `roofline` is the dominant kernel (FC1 grouped GEMM):
 algorithmic bytes per launch over its average duration, measured here with
 HIP events around that step on the stream it runs on. `cpu_baseline` times
 the CPU oracle on a bounded sample (all routes of the first --cpu-experts
-experts).
+experts). `device` reports this device's own ceilings: the bandwidth of a plain
+1 GiB device-to-device copy and of a full read (reduction) of it, and the
+graphics clock and socket power sampled while the step runs back to back.
 """
 import argparse
 import json
@@ -31,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-MoE tokens/s + effective TFLOPS (% MFMA peak), H7168/I3072 top-6, 1 GPU"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense FP16/BF16 MFMA
+NOMINAL_MHZ = 2400.0         # MI355X peak engine clock the MFMA peak is quoted at
 NVFP4_BYTES = 9.0 / 16.0     # packed E2M1 + one E4M3 scale per 16 elements
 
 
@@ -97,6 +100,87 @@ def cpu_baseline(w, ids, wts, n_experts):
             "sample": f"all {rows} routes of experts {experts} (of T*K={w.T * w.K}) incl. per-token "
                       f"quantization of all {w.T} tokens; tokens/s = routes/K/s; {dt:.1f} s",
             "seconds": dt}
+
+
+def stream_gbs(torch, nbytes=1 << 30, reps=10):
+    """Achievable streaming bandwidth of this device (next to the 8 TB/s nominal peak):
+    bytes read + written per second by a plain device-to-device copy, and bytes read per
+    second by a full reduction (torch's amax) of the same buffer."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    copy = 2.0 * nbytes / timed(lambda: dst.copy_(src)) / 1e9
+    read = nbytes / timed(lambda: torch.amax(src)) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return copy, read
+
+
+def clock_under_load(torch, fn, seconds=1.0):
+    """Median graphics clock (MHz) and socket power (W) sampled from the GPU's metrics table
+    while fn() runs back to back for about `seconds`; None where the metrics are unavailable."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as exc:  # no metrics interface: report the gap, do not guess
+        return {"gfx_mhz": None, "socket_w": None, "samples": 0, "note": f"amdsmi unavailable: {exc}"}
+
+    def num(v):
+        if isinstance(v, (list, tuple)):
+            v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 65535]
+            return sum(v) / len(v) if v else None
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 65535 else None
+
+    clocks, watts, stop = [], [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                c = num(m.get("current_gfxclks")) or num(m.get("current_gfxclk")) or \
+                    num(m.get("average_gfxclk_frequency"))
+                pw = num(m.get("current_socket_power")) or num(m.get("average_socket_power"))
+                if c:
+                    clocks.append(c)
+                if pw:
+                    watts.append(pw)
+            except Exception:
+                pass
+            stop.wait(0.01)
+
+    for _ in range(20):
+        fn()
+    torch.cuda.synchronize()
+    t = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    med = lambda v: float(np.median(v)) if v else None
+    return {"gfx_mhz": med(clocks), "socket_w": med(watts), "samples": len(clocks),
+            "note": "amdsmi GPU metrics, median over the samples taken while the step ran"}
 
 
 def main():
@@ -269,16 +353,28 @@ def main():
     recipes["determinism_cost"] = (recipes["per_token_ordered_finalize"]["ms_per_step"] /
                                    recipes["per_token_fused_finalize"]["ms_per_step"] - 1.0)
     del P_pt
+
+    # ---------------------------------------------------------------- ceilings of this device
+    copy_gbs, read_gbs = stream_gbs(torch)
+    clock = clock_under_load(torch, step)
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s, read {read_gbs:.0f} GB/s; "
+        f"clock under load {clock['gfx_mhz']} MHz, "
+        f"{clock['socket_w']} W ({clock['samples']} samples)")
+
     counts = np.diff(views["expert_offsets"].cpu().numpy())
     R = int(counts.sum())
     ab = algorithmic_bytes(w, counts, T, R)
     kernels = {n: {"us": float(stage_ms[i] * 1e3),
                    "GB/s": float(ab[n] / (stage_ms[i] * 1e-3) / 1e9)} for i, n in enumerate(names)}
+    for k in kernels.values():
+        k["hbm_frac"] = k["GB/s"] / PEAK_HBM_GBS
     flops = 2.0 * R * (w.N1 * w.H + w.H * w.I)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     fc1_flops = 2.0 * R * w.N1 * w.H
     kernels["fc1"]["TFLOP/s"] = float(fc1_flops / (stage_ms[2] * 1e-3) / 1e12)
     kernels["fc2"]["TFLOP/s"] = float(2.0 * R * w.H * w.I / (stage_ms[4] * 1e-3) / 1e12)
+    for n in ("fc1", "fc2"):
+        kernels[n]["mfma_frac"] = kernels[n]["TFLOP/s"] / PEAK_F16_TFLOPS
     fc1_gbs = ab["fc1"] / (fc1_ms_timed * 1e-3) / 1e9
     traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", f"fc1_{w.name}_hbm_traffic.txt"), w.name)
 
@@ -304,7 +400,14 @@ def main():
                      "fc1 grouped GEMM (squared-ReLU epilogue)",
                      "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3},
+                     "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3,
+                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": fc1_gbs / copy_gbs,
+                     "device_read_GBps": read_gbs, "frac_of_device_read": fc1_gbs / read_gbs},
+        "device": {"copy_GBps": copy_gbs, "read_GBps": read_gbs, "gfx_mhz_under_load": clock["gfx_mhz"],
+                   "socket_w_under_load": clock["socket_w"], "clock_samples": clock["samples"],
+                   "clock_note": clock["note"], "nominal_mhz": NOMINAL_MHZ,
+                   "mfma_frac_at_measured_clock": (tflops / (PEAK_F16_TFLOPS * clock["gfx_mhz"] / NOMINAL_MHZ)
+                                                   if clock["gfx_mhz"] else None)},
         "kernels": kernels,
         "prepare": prepare,
         "recipes": recipes,

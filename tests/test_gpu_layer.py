@@ -277,3 +277,39 @@ def test_forward_matches_oracle(pm):
     got = pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P)
     _sync()
     _assert_rows_close(bf16_bits(got), _oracle(w, x, ids, wts).out, "forward")
+
+
+@pytest.mark.parametrize("recipe", ["per_token", "per_tensor", "w4a16"])
+def test_forward_edges(pm, recipe):
+    """pmoe_moe_forward with int64 ids, an expert offset and -1 fills, and with T = 1,
+    bit for bit against the separate quantize + pmoe_routed_moe_ex path."""
+    import torch
+    w = synth.WORKLOADS["swiglu"]
+    x = synth.activations(w)
+    ids, wts = synth.router(w)
+    ids = ids.astype(np.int64) + 40
+    ids[3, :] = -1
+    ids[7, 2] = 40 + w.E
+    xd = dev_bf16(x)
+    a1 = torch.tensor([float(2688.0 / np.abs(bf16_to_f32(x)).max())], device="cuda")
+    a2 = torch.tensor([2688.0 / 0.5], dtype=torch.float32, device="cuda")
+    scales = (a1, a2) if recipe == "per_tensor" else None
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"), input_scales=scales)
+    kw = dict(recipe=recipe, a2=a2 if recipe == "per_tensor" else None, expert_offset=40)
+    fa1 = a1 if recipe == "per_tensor" else None
+    for rows in (slice(None), slice(5, 6)):
+        xs = xd[rows].contiguous()
+        if recipe == "per_token":
+            xin = pm.quantize_input_per_token(xs)
+        elif recipe == "per_tensor":
+            xin = pm.quantize_input_per_tensor(xs, a1) + (None,)
+        else:
+            xin = (xs, None, None)
+        i_d, w_d = dev(ids[rows]), dev(wts[rows])
+        ref = pm.routed_moe_ex(*xin, i_d, w_d, P, **kw)
+        got = pm.moe_forward(xs, i_d, w_d, P, a1=fa1, **kw)
+        _sync()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    full = pm.moe_forward(xd, dev(ids), dev(wts), P, a1=fa1, **kw)
+    _sync()
+    assert not bf16_bits(full)[3].any()            # a token without valid routes gets +0
