@@ -68,17 +68,30 @@ __global__ __launch_bounds__(256) void route_count_kernel(const IdT* __restrict_
 }
 
 // Inclusive block scan over 1024 threads (Hillis-Steele in LDS).
+// Inclusive prefix sum over the 1024 threads of a workgroup; the total is left
+// in sh[1023]. Each wave scans its 64 values with shuffles, then adds the
+// totals of the waves before it (two barriers instead of twenty).
 __device__ __forceinline__ int block_inclusive_scan_1024(int v, int* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  return sh[tid];
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int t = sh[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();  // every wave has read sh[0..15]
+  if (tid == 1023) sh[1023] = total;
+  __syncthreads();
+  return x + before;
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ block_counts, int NB,
