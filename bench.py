@@ -16,8 +16,8 @@ algorithmic bytes per launch over its average duration, measured here with
 HIP events around that step on the stream it runs on. `cpu_baseline` times
 the CPU oracle on a bounded sample (all routes of the first --cpu-experts
 experts). `device` reports this device's own ceilings: the bandwidth of a plain
-1 GiB device-to-device copy and of a full read (reduction) of it, and the
-graphics clock and socket power sampled while the step runs back to back.
+1 GiB device-to-device copy, and the graphics clock and socket power sampled
+while the step runs back to back.
 """
 import argparse
 import json
@@ -102,30 +102,24 @@ def cpu_baseline(w, ids, wts, n_experts):
             "seconds": dt}
 
 
-def stream_gbs(torch, nbytes=1 << 30, reps=10):
-    """Achievable streaming bandwidth of this device (next to the 8 TB/s nominal peak):
-    bytes read + written per second by a plain device-to-device copy, and bytes read per
-    second by a full reduction (torch's amax) of the same buffer."""
+def stream_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Bytes read + written per second by a plain 1 GiB device-to-device copy: the
+    achievable streaming bandwidth of this device, next to the 8 TB/s nominal peak."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
-
-    copy = 2.0 * nbytes / timed(lambda: dst.copy_(src)) / 1e9
-    read = nbytes / timed(lambda: torch.amax(src)) / 1e9
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
-    return copy, read
+    return gbs
 
 
 def clock_under_load(torch, fn, seconds=1.0):
@@ -355,10 +349,9 @@ def main():
     del P_pt
 
     # ---------------------------------------------------------------- ceilings of this device
-    copy_gbs, read_gbs = stream_gbs(torch)
+    copy_gbs = stream_copy_gbs(torch)
     clock = clock_under_load(torch, step)
-    log(f"[bench] device copy {copy_gbs:.0f} GB/s, read {read_gbs:.0f} GB/s; "
-        f"clock under load {clock['gfx_mhz']} MHz, "
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s; clock under load {clock['gfx_mhz']} MHz, "
         f"{clock['socket_w']} W ({clock['samples']} samples)")
 
     counts = np.diff(views["expert_offsets"].cpu().numpy())
@@ -401,9 +394,8 @@ def main():
                      "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3,
-                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": fc1_gbs / copy_gbs,
-                     "device_read_GBps": read_gbs, "frac_of_device_read": fc1_gbs / read_gbs},
-        "device": {"copy_GBps": copy_gbs, "read_GBps": read_gbs, "gfx_mhz_under_load": clock["gfx_mhz"],
+                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": fc1_gbs / copy_gbs},
+        "device": {"copy_GBps": copy_gbs, "gfx_mhz_under_load": clock["gfx_mhz"],
                    "socket_w_under_load": clock["socket_w"], "clock_samples": clock["samples"],
                    "clock_note": clock["note"], "nominal_mhz": NOMINAL_MHZ,
                    "mfma_frac_at_measured_clock": (tflops / (PEAK_F16_TFLOPS * clock["gfx_mhz"] / NOMINAL_MHZ)
