@@ -1,7 +1,9 @@
 // C ABI of the pmoe library: host-side validation and launch sequencing.
 // No kernel lives here. Every entry point validates all of its arguments on
-// the host before the first launch, enqueues on the caller's stream, and
-// never allocates device memory or synchronizes.
+// the host before the first launch, enqueues on the caller's stream (the
+// routed-MoE calls also on one library-owned second stream per device, forked
+// from and joined back into the caller's), and never allocates device memory
+// for data or synchronizes with the host.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -325,15 +327,26 @@ struct Aux {
 std::mutex g_aux_mu;
 Aux g_aux[64];
 
+// The current device's Aux, created on first use. Call with g_aux_mu held.
+// Either all three objects exist afterwards or none is kept (a failed
+// creation is reported and retried on the next call).
 int aux_for_current_device(Aux** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
     return fail(PMOE_ERR_DEVICE, "no usable current device");
   Aux& a = g_aux[dev];
   if (!a.s2) {
-    PMOE_HIP(hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking));
-    PMOE_HIP(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
-    PMOE_HIP(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+    Aux n;
+    hipError_t e = hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s2) (void)hipStreamDestroy(n.s2);
+      return fail(PMOE_ERR_HIP, std::string("creating the second stream: ") + hipGetErrorString(e));
+    }
+    a = n;
   }
   *out = &a;
   return PMOE_OK;
@@ -408,9 +421,9 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
     uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
     float* wsc = reinterpret_cast<float*>(base + L.x_scale);
+    std::lock_guard<std::mutex> lock(g_aux_mu);
     Aux* aux = nullptr;
     PMOE_TRY(aux_for_current_device(&aux));
-    std::lock_guard<std::mutex> lock(g_aux_mu);
     PMOE_HIP(hipEventRecord(aux->fork, s));
     PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
     PMOE_HIP(launch_quantize_bf16(x, T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, aux->s2));
@@ -497,9 +510,9 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   const bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
                      (streams == 2 || (streams == 0 && TK >= 2048));
   if (split) {
+    std::lock_guard<std::mutex> lock(g_aux_mu);
     Aux* aux = nullptr;
     PMOE_TRY(aux_for_current_device(&aux));
-    std::lock_guard<std::mutex> lock(g_aux_mu);
     PMOE_HIP(hipEventRecord(aux->fork, s));
     PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
     PMOE_TRY(chain(1, s, true, true, true));
