@@ -1,0 +1,65 @@
+"""GPU parity at the largest supported sizes: rows of 16384 elements for both
+quantizers (bit-exact), and the routed path with the longest reduction
+(H = 16384) and the widest FC1 (SwiGLU with I = 16384, N1 = 32768) against
+the oracle, to the per-token tolerance (1e-2 of the token's max)."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import bf16_bits, dev, dev_bf16
+from oracle import moe as om
+from oracle import quant as oq
+from oracle.formats import bf16_to_f32
+
+pytestmark = pytest.mark.gpu
+MAX_ROW = 16384
+
+
+@pytest.fixture(scope="module")
+def pm():
+    import torch
+    import precision_moe_amd as pm
+    assert torch.cuda.is_available()
+    return pm
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def test_quantize_longest_rows(pm):
+    rng = np.random.default_rng(16384)
+    x = rng.standard_normal((7, MAX_ROW)).astype(np.float32)
+    x[1, ::97] *= 50.0                                  # outliers
+    x[2] = 0.0                                          # an all-zero row
+    xb = synth._bf16_np(x)
+    xq, xs, xg = pm.quantize_input_per_token(dev_bf16(xb))
+    h = (rng.standard_normal((5, MAX_ROW)) * np.exp(rng.uniform(-8, 8, (5, 1)))).astype(np.float32)
+    hq, hs, hg = pm.quantize_rows_f32(dev(h))
+    _sync()
+    for got, want in zip((xq, xs, xg, hq, hs, hg),
+                         oq.quantize_input_per_token(xb) + oq.quantize_rows_f32(h)):
+        got = got.cpu().numpy()
+        assert got.shape == want.shape and np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+@pytest.mark.parametrize("H,I,act", [(MAX_ROW, 64, "relu2"), (64, MAX_ROW, "swiglu")])
+def test_moe_largest_dims(pm, H, I, act):
+    rng = np.random.default_rng(H + I)
+    T, K, E = 9, 2, 3
+    N1 = 2 * I if act == "swiglu" else I
+    w1 = synth._bf16_np(rng.standard_normal((E, N1, H)).astype(np.float32) * 0.02)
+    w2 = synth._bf16_np(rng.standard_normal((E, H, I)).astype(np.float32) * 0.02)
+    x = synth._bf16_np(rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    wts = rng.uniform(0.1, 1.0, (T, K)).astype(np.float32)
+    P = pm.prepare_weights(dev_bf16(w1), dev_bf16(w2))
+    out = pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P)
+    _sync()
+    xq, xs, xg = oq.quantize_input_per_token(x)
+    res = om.routed_moe(xq, xs, xg, ids, wts, om.prepare_weights(w1, w2), act)
+    got = bf16_to_f32(bf16_bits(out)).astype(np.float64)
+    want = bf16_to_f32(res.out).astype(np.float64)
+    err = np.abs(got - want).max(axis=1)
+    assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
