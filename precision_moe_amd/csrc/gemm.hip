@@ -22,7 +22,7 @@
 //     9 KB slab, so a workgroup streams a single sequential region; per chunk
 //     and position each lane loads one 16-byte span (1 KB per wave-load) and
 //     one dword of four E4M3 scales, by buffer loads with scalar chunk
-//     offsets. Loads run kRing - 1 chunks ahead in a register ring; decoding
+//     offsets. Loads run 3 (or 1) chunks ahead in a register ring; decoding
 //     happens in registers straight into MFMA operand order (each block scale
 //     multiplied into its 16 decoded values, exact in FP16), and every decoded
 //     B fragment feeds all row blocks.
@@ -58,16 +58,18 @@ constexpr int kStageK = 128;                       // reduction elements per LDS
 constexpr int kLdsRow = kStageK * 2;               // bytes per LDS A row (16 slots of 16 B)
 constexpr int kLdsStage = kTileM * kLdsRow;        // bytes per LDS stage buffer
 constexpr int kBufFlags = 0x00020000;              // raw buffer, 32-bit data format
-#ifndef PMOE_GEMM_RING
-#define PMOE_GEMM_RING 4
-#endif
-#ifndef PMOE_GEMM_WG_PER_CU
-#define PMOE_GEMM_WG_PER_CU 2
-#endif
-constexpr int kRing = PMOE_GEMM_RING;              // B register ring slots per wave (even)
-constexpr int kGroup = kRing / 2;                  // stages per loop iteration
-constexpr int kStages = (kGroup % 2) ? 3 : 2;      // LDS A stage buffers
-constexpr int kPrefetch = kRing - 1;               // B chunks in flight ahead of the one in use
+constexpr int kGroup = 2;                          // stages per loop iteration
+constexpr int kStages = 2;                         // LDS A stage buffers (double buffer)
+// B register ring (chunks per wave, RING - 1 of them in flight) and resident
+// workgroups per CU. A whole-expert-set launch keeps 4 chunks in flight at 2
+// workgroups per CU (180 VGPRs). The half launches of the NVFP4 recipes run
+// two at a time on two streams; there a ring of 2 (168 VGPRs) lets 3
+// workgroups share a CU, which fills the CUs better than a deeper ring.
+template <int AK, bool HALF>
+struct FcConfig {
+  static constexpr int kRing = (HALF && AK == 0) ? 2 : 4;
+  static constexpr int kWgPerCu = (HALF && AK == 0) ? 3 : 2;
+};
 
 __host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
 
@@ -112,7 +114,7 @@ struct BFrag {
 // load inside the loop is unconditional (addresses past the end are out of the
 // buffer range and return zeros, and that data is never used), which keeps the
 // in-order load counters exact so the B ring really stays in flight.
-template <int MODE, int NRB, int AK>
+template <int MODE, int NRB, int AK, int kRing>
 __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
                                         int mrows, int nt) {
@@ -221,6 +223,8 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   // (c + kPrefetch) % kRing -- the slot chunk c - 1 has just finished
   // decoding -- with chunk c + kPrefetch, so each slot keeps its registers
   // around the loop and kPrefetch chunks stay in flight.
+  static_assert(kRing == 2 || kRing == 4, "the stage loop assumes a ring of 2 or 4 chunks");
+  constexpr int kPrefetch = kRing - 1;  // B chunks in flight ahead of the one in use
   uint4 rq0[kRing], rq1[kRing];
   uint32_t rs0[kRing], rs1[kRing];
 #pragma unroll
@@ -290,23 +294,24 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     __syncthreads();
   };
 
-  // The loop body covers kGroup stages (kRing chunks): stage j of a group uses
-  // LDS buffer j % kStages and ring slots 2j, 2j+1, so every index is a
-  // compile-time constant after unrolling.
+  // The loop body covers two stages (four chunks): stage j of a pair uses LDS
+  // buffer j and ring slots (2j) % kRing and the next one, so every index is
+  // a compile-time constant after unrolling (st is even, so chunk c sits in
+  // slot c % kRing as the ring requires).
   const int nfull = KC >> 1;  // stages holding two chunks
   int st = 0;
   for (; st + kGroup <= nfull; st += kGroup) {
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) stage(st + j, j % kStages, 2 * j);
+    for (int j = 0; j < kGroup; ++j) stage(st + j, j, (2 * j) % kRing);
   }
   const int rem = nfull - st;  // remaining full stages, fewer than kGroup
 #pragma unroll
   for (int j = 0; j < kGroup - 1; ++j)
-    if (j < rem) stage(st + j, j % kStages, 2 * j);
+    if (j < rem) stage(st + j, j, (2 * j) % kRing);
   if (KC & 1) {  // final half stage: chunk KC-1 = 2*nfull, group position rem
 #pragma unroll
     for (int j = 0; j < kGroup; ++j)
-      if (j == rem) chunk(2 * nfull, &a_lds[j % kStages][0], 0, 2 * j);
+      if (j == rem) chunk(2 * nfull, &a_lds[j][0], 0, (2 * j) % kRing);
   }
 
   // ------------------------------------------------------------------ epilogue
@@ -372,7 +377,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   }
 }
 
-template <int MODE, int AK>
+template <int MODE, int AK, int kRing>
 __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                          int* a_row, float* s_row) {
   const int tid = threadIdx.x;
@@ -407,30 +412,30 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
   }
   __syncthreads();
   switch ((mrows + 15) >> 4) {  // 16-row blocks that hold rows of this tile
-    case 1: fc_tile<MODE, 1, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    case 2: fc_tile<MODE, 2, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    case 3: fc_tile<MODE, 3, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    default: fc_tile<MODE, 4, AK>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 1: fc_tile<MODE, 1, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 2: fc_tile<MODE, 2, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 3: fc_tile<MODE, 3, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    default: fc_tile<MODE, 4, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
   }
 }
 
 // One launch over the tiles of every local expert.
 template <int MODE, int AK>
-__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_kernel(FcParams P) {
+__global__ __launch_bounds__(kThreads, (FcConfig<AK, false>::kWgPerCu)) void fc_kernel(FcParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
   __shared__ float s_row[kTileM];
-  fc_block<MODE, AK>(P, a_lds, a_row, s_row);
+  fc_block<MODE, AK, FcConfig<AK, false>::kRing>(P, a_lds, a_row, s_row);
 }
 
 // The same code over one half of the experts (P.part = 1 or 2); a kernel of
 // its own name so that a trace tells the half launches from the whole ones.
 template <int MODE, int AK>
-__global__ __launch_bounds__(kThreads, PMOE_GEMM_WG_PER_CU) void fc_half_kernel(FcParams P) {
+__global__ __launch_bounds__(kThreads, (FcConfig<AK, true>::kWgPerCu)) void fc_half_kernel(FcParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
   __shared__ float s_row[kTileM];
-  fc_block<MODE, AK>(P, a_lds, a_row, s_row);
+  fc_block<MODE, AK, FcConfig<AK, true>::kRing>(P, a_lds, a_row, s_row);
 }
 
 template <int MODE, int AK>
