@@ -69,8 +69,9 @@ extern "C" {
 /* Library version (major*10000 + minor*100 + patch). */
 int pmoe_version(void);
 
-/* Message of the last error returned on this host thread ("" if none). The
- * pointer stays valid until the next pmoe call on the same thread. */
+/* Message of the last error returned on this host thread: "" after a call
+ * that succeeded. The pointer stays valid until the next pmoe call on the
+ * same thread. */
 const char* pmoe_last_error(void);
 
 /* ============================================================ prepared weights

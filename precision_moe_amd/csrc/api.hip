@@ -186,6 +186,7 @@ PMOE_EXPORT int pmoe_weight_bytes(int E, int N1, int H, int I, size_t sizes[4]) 
 
 PMOE_EXPORT size_t pmoe_prepare_workspace_bytes(int E, int N1, int H, int I) {
   if (check_weight_shape(E, N1, H, I) != PMOE_OK) return 0;
+  ok();
   return prepare_ws(E, N1, H, I);
 }
 
@@ -297,6 +298,7 @@ PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, v
 
 PMOE_EXPORT size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act) {
   if (check_moe_shape(T, K, E, H, I, act) != PMOE_OK) return 0;
+  ok();
   return moe_layout(T, K, E, H, I).total;
 }
 

@@ -42,3 +42,41 @@ def test_c_program_calls_the_library(tmp_path, libdir):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_smoke: ok" in r.stdout
+
+
+LLVM_BIN = "/opt/rocm/llvm/bin"
+HIPCC = "/opt/rocm/bin/hipcc"
+
+
+@pytest.mark.skipif(not (os.path.exists(os.path.join(LLVM_BIN, "clang")) and os.path.exists(HIPCC)),
+                    reason="needs the ROCm clang toolchain")
+def test_c_program_under_host_sanitizers(tmp_path, libdir):
+    """The host layer of the library (argument checks, layouts, error strings) built with
+    AddressSanitizer and UndefinedBehaviorSanitizer on the host side only, linked with the
+    other objects of the normal build, driven by the same C program."""
+    from precision_moe_amd import build as pb
+    objs = sorted(os.path.join(pb.BUILD, f) for f in os.listdir(pb.BUILD)
+                  if f.endswith(".o") and f != "api.o") if os.path.isdir(pb.BUILD) else []
+    if len(objs) != len(pb.SOURCES) - 1:
+        pytest.fail("the library's objects are missing: build it first")
+    api = tmp_path / "api_san.o"
+    lib = tmp_path / "libpmoe_san.so"
+    exe = tmp_path / "abi_smoke_san"
+    rt = os.path.dirname(subprocess.run(
+        [os.path.join(LLVM_BIN, "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+        capture_output=True, text=True, check=True).stdout.strip())
+    subprocess.run([HIPCC, *pb.FLAGS, "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                    "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                    "-c", os.path.join(pb.CSRC, "api.hip"), "-o", str(api)],
+                   check=True, capture_output=True)
+    san = "-fsanitize=" + "address,undefined"
+    subprocess.run([os.path.join(LLVM_BIN, "clang++"), "-shared", "-fPIC", san, "-shared-libsan",
+                    "-o", str(lib), str(api), *objs, "-L/opt/rocm/lib", "-lamdhip64",
+                    "-Wl,-rpath,/opt/rocm/lib"], check=True)
+    subprocess.run([os.path.join(LLVM_BIN, "clang"), "-std=c99", san, "-shared-libsan", "-I", INC,
+                    SRC, "-o", str(exe), "-L", str(tmp_path), "-lpmoe_san",
+                    f"-Wl,-rpath,{tmp_path}", f"-Wl,-rpath,{rt}"], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_smoke: ok" in r.stdout and "runtime error" not in r.stderr
