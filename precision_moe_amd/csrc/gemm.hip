@@ -34,6 +34,8 @@
 //   and up column blocks of one output sit in the same wave), optionally with
 //   the clamp gate <= L, -L <= up <= L;  FC2: bf16(y);  FC2 with the fused
 //   finalize: FP32 atomic add of w * y into the token's row (order-free).
+// Outputs other than the atomic adds go through the freed A-stage LDS so that
+// each wave writes whole 16-byte pieces of its (contiguous) output columns.
 //
 // Batch invariance: every output element is one chain of MFMAs over k in fixed
 // order whatever T, the tile or the other rows are; no split-K.
@@ -315,64 +317,103 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   }
 
   // ------------------------------------------------------------------ epilogue
+  // The barrier ends every wave's reads of the A stages, which the staged
+  // stores below reuse.
+  __syncthreads();
   // acc[rb][cb][i] is row 16*rb + 4*(lane/16) + i, column 16*cb + lane%16 of
   // the wave's 64 columns: position p0 + cb/2, half h = cb%2.
   const bool use0 = p0 < NB, use1 = p0 + 1 < NB;
   const int n16 = lane & 15;
-  // FC1 writes the FP32 activation output (NVFP4 path: it is requantized next)
-  // or its BF16 rounding (W4A16: it is FC2's input as it is).
-  auto store_h = [&](long idx, float h) {
-    if constexpr (AK == 1)
-      static_cast<uint16_t*>(P.out)[idx] = (uint16_t)f32_to_bf16(h);
-    else
-      static_cast<float*>(P.out)[idx] = h;
-  };
+  if constexpr (MODE == kFc2Fused) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * rb + 4 * (lane >> 4) + i;
-      if (m >= mrows) continue;
-      const float s = s_row[m];
-      const long orow = (long)(row0 + m) * P.out_stride;
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * rb + 4 * (lane >> 4) + i;
+        if (m >= mrows) continue;
+        const float s = s_row[m];
+        // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
+        const int f = P.out_route[row0 + m];
+        const float wgt = P.out_w[f];
+        float* acc_row = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float c0 = acc[rb][h][i], c1 = acc[rb][2 + h][i];  // positions p0, p0 + 1
-        const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
-        if constexpr (MODE == kFc1Relu2) {
-          if (use0) {
-            const float y = __builtin_fmaxf(c0 * s, 0.0f);
-            store_h(orow + col0, y * y);
-          }
-          if (use1) {
-            const float y = __builtin_fmaxf(c1 * s, 0.0f);
-            store_h(orow + col1, y * y);
-          }
-        } else if constexpr (MODE == kFc1Swiglu) {
-          // p0 is even: position p0 holds gate rows, p0 + 1 the matching up rows.
-          if (use0) {
-            float g = c0 * s;
-            float u = c1 * s;
-            if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
-              g = __builtin_fminf(g, P.swiglu_limit);
-              u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
-            }
-            const float silu = g / (1.0f + expf(-g));
-            store_h(orow + kColBlock * (p0 >> 1) + 16 * h + n16, silu * u);
-          }
-        } else if constexpr (MODE == kFc2Fused) {
-          // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
-          const int f = P.out_route[row0 + m];
-          const float wgt = P.out_w[f];
-          float* acc_row = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
-          if (use0) unsafeAtomicAdd(acc_row + col0, wgt * (c0 * s));
-          if (use1) unsafeAtomicAdd(acc_row + col1, wgt * (c1 * s));
-        } else {
-          uint16_t* out = static_cast<uint16_t*>(P.out) + orow;
-          if (use0) out[col0] = (uint16_t)f32_to_bf16(c0 * s);
-          if (use1) out[col1] = (uint16_t)f32_to_bf16(c1 * s);
+        for (int h = 0; h < 2; ++h) {
+          const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
+          if (use0) unsafeAtomicAdd(acc_row + col0, wgt * (acc[rb][h][i] * s));
+          if (use1) unsafeAtomicAdd(acc_row + col1, wgt * (acc[rb][2 + h][i] * s));
         }
       }
+    }
+  } else {
+    // Staged stores: each wave writes its part of the output tile into its own
+    // 8 KB of the (now free) A stage memory, then copies it out in 16-byte
+    // row-contiguous pieces. The wave's output columns are contiguous: 64
+    // (squared ReLU, FC2) or 32 (SwiGLU: gate and up fold into one). FC1
+    // writes FP32 h for the NVFP4 recipes (requantized next) and BF16 h for
+    // W4A16 (FC2's input as it is); FC2 writes BF16 z.
+    constexpr bool kSwiglu = MODE == kFc1Swiglu;
+    constexpr int kS = (MODE == kFc2 || AK == 1) ? 2 : 4;           // bytes per element
+    constexpr int kCw = kSwiglu ? 32 : 64;                          // columns per wave
+    constexpr int kRowB = kCw * kS;                                 // LDS bytes per row
+    constexpr int kPassRows = (8192 / kRowB) < kTileM ? 8192 / kRowB : kTileM;
+    uint8_t* wbuf = &a_lds[0][0] + wave * 8192;
+    const long col_base = kSwiglu ? (long)kColBlock * (p0 >> 1) : (long)kColBlock * p0;
+    // bytes of an LDS row that exist in the output: padding positions past NB are dropped
+    const int row_bytes = kSwiglu ? (use0 ? kRowB : 0) : (use1 ? kRowB : (use0 ? kRowB / 2 : 0));
+    auto put = [&](int m, int lc, float v) {
+      if constexpr (kS == 2)
+        *reinterpret_cast<uint16_t*>(wbuf + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(v);
+      else
+        *reinterpret_cast<float*>(wbuf + m * kRowB + lc * 4) = v;
+    };
+#pragma unroll
+    for (int r_lo = 0; r_lo < 16 * NRB; r_lo += kPassRows) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (16 * rb + 16 <= r_lo || 16 * rb >= r_lo + kPassRows) continue;  // resolved at compile time
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * rb + 4 * (lane >> 4) + i;
+          if (m >= mrows) continue;
+          const float s = s_row[m];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float c0 = acc[rb][h][i], c1 = acc[rb][2 + h][i];  // positions p0, p0 + 1
+            const int lc = 16 * h + n16;
+            if constexpr (MODE == kFc1Relu2) {
+              const float y0 = __builtin_fmaxf(c0 * s, 0.0f);
+              const float y1 = __builtin_fmaxf(c1 * s, 0.0f);
+              put(m - r_lo, lc, y0 * y0);
+              put(m - r_lo, lc + kColBlock, y1 * y1);
+            } else if constexpr (kSwiglu) {
+              // p0 is even: position p0 holds gate rows, p0 + 1 the matching up rows.
+              float g = c0 * s;
+              float u = c1 * s;
+              if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
+                g = __builtin_fminf(g, P.swiglu_limit);
+                u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
+              }
+              const float silu = g / (1.0f + expf(-g));
+              put(m - r_lo, lc, silu * u);
+            } else {
+              put(m - r_lo, lc, c0 * s);
+              put(m - r_lo, lc + kColBlock, c1 * s);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int nrow = min(kPassRows, mrows - r_lo);
+      uint8_t* out = static_cast<uint8_t*>(P.out) + ((long)(row0 + r_lo) * P.out_stride + col_base) * kS;
+#pragma unroll
+      for (int k = 0; k < kPassRows * kRowB / (64 * 16); ++k) {
+        const int off = (k * 64 + lane) * 16;
+        const int r = off / kRowB, cb = off % kRowB;
+        if (r < nrow && cb < row_bytes)
+          *reinterpret_cast<uint4*>(out + (long)r * P.out_stride * kS + cb) =
+              *reinterpret_cast<const uint4*>(wbuf + off);
+      }
+      if (r_lo + kPassRows < 16 * NRB) __syncthreads();  // the next pass overwrites the buffer
     }
   }
 }
@@ -394,14 +435,16 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
   if (j >= per) return;
   const int item = t_lo * NT + (blockIdx.x & 7) * per + j;
   if (item >= t_hi * NT) return;
-  const int4 ta = reinterpret_cast<const int4*>(P.tiles)[item / NT];  // a tile of the item's expert
-  const int first = ta.z, count = ta.w;
+  // Every tile entry of an expert holds {expert, its first row, its first
+  // tile, its row count}: one load gives the item's rows.
+  const int4 ta = reinterpret_cast<const int4*>(P.tiles)[item / NT];
+  const int e = ta.x, first = ta.z, rows_e = ta.w;
+  const int count = (rows_e + kTileM - 1) / kTileM;
   const int local = item - first * NT;
   const int nt = local / count;
-  const int4 td = reinterpret_cast<const int4*>(P.tiles)[first + (local - nt * count)];
-  const int e = td.x;
-  const int row0 = P.expert_offsets[e] + td.y;
-  const int mrows = min(kTileM, P.expert_offsets[e + 1] - row0);
+  const int m_tile = local - nt * count;
+  const int row0 = ta.y + m_tile * kTileM;
+  const int mrows = min(kTileM, rows_e - m_tile * kTileM);
 
   if (tid < kTileM) {
     const int r = row0 + min(tid, mrows - 1);  // rows past the tile end repeat a valid row

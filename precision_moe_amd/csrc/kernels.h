@@ -40,7 +40,8 @@ struct RouteBuffers {
   int* rank_local;      // [TK]
   int* block_counts;    // [route blocks][E]
   int* expert_offsets;  // [E+1]
-  int* tiles;           // [max_tiles][4] = {expert, first local row, expert's first tile, expert's tiles}
+  int* tiles;           // [max_tiles][4]: every M-tile of expert e holds {e, e's first row,
+                        // e's first tile, e's row count}; tiles are grouped by expert
   int* counters;        // [4] = {R, tiles, tiles of experts < ceil(E/2), rows of those experts}
   int* row_of_route;    // [TK]
   int* route_of_row;    // [TK]

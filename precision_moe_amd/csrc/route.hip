@@ -11,9 +11,10 @@
 //                   per-expert counts.
 //   route_scan    : one workgroup: per expert, exclusive prefix over blocks
 //                   (in place), totals, exclusive scan over experts, the
-//                   M-tile list {expert, first local row, expert's first
-//                   tile, expert's tile count} (tiles of 64 rows, grouped by
-//                   expert in expert order), and where the first half of the
+//                   M-tile list (tiles of 64 rows, grouped by expert in
+//                   expert order; every tile of an expert holds {expert, its
+//                   first row, its first tile, its row count}), and where the
+//                   first half of the
 //                   experts ends in tiles and rows (counters[2], counters[3]),
 //                   for running the two halves on two streams.
 //   route_scatter : row = expert start + block prefix + in-block rank;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ bloc
     expert_offsets[e] = start;
     for (int i = 0; i < ntiles; ++i) {
       int4* t = reinterpret_cast<int4*>(tiles) + tstart + i;
-      *t = make_int4(e, i * kTileM, tstart, ntiles);
+      *t = make_int4(e, start, tstart, total);
     }
   }
   if (e == 0) {
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     expert_offsets[tid] = start;
     base[tid] = start;
     for (int i = 0; i < ntiles; ++i)
-      reinterpret_cast<int4*>(tiles)[tstart + i] = make_int4(tid, i * kTileM, tstart, ntiles);
+      reinterpret_cast<int4*>(tiles)[tstart + i] = make_int4(tid, start, tstart, total);
   }
   if (tid == 0) {
     expert_offsets[E] = R;
