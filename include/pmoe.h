@@ -208,7 +208,8 @@ size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act);
 #define PMOE_WS_ROW_OF_ROUTE 0   /* int32 [T*K]   expert-sorted row of route t*K+j, -1 if invalid */
 #define PMOE_WS_ROUTE_OF_ROW 1   /* int32 [T*K]   route index of each row (first R valid)        */
 #define PMOE_WS_EXPERT_OFFSETS 2 /* int32 [E+1]   first row of each local expert; [E] = R          */
-#define PMOE_WS_COUNTERS 3       /* int32 [4]     {R, number of M-tiles, 0, 0}                     */
+#define PMOE_WS_COUNTERS 3       /* int32 [4]     {R, number of M-tiles, first M-tile and first row
+                                    of the experts run on the second stream}                    */
 #define PMOE_WS_H 4              /* float32 [T*K, I]   activation output (rows < R valid);
                                     BF16 [T*K, I] under pmoe_routed_moe_w4a16                   */
 #define PMOE_WS_HQ 5             /* uint8 [T*K, I/2]   requantized intermediate codes              */

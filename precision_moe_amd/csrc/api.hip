@@ -316,21 +316,22 @@ namespace {
 enum Recipe { kPerToken = PMOE_RECIPE_PER_TOKEN, kPerTensor = PMOE_RECIPE_PER_TENSOR,
               kW4A16 = PMOE_RECIPE_W4A16 };
 
-// A second stream and a fork / join event pair per device, created on first
-// use and kept until the process ends: the two halves of the experts run their
-// FC1 -> requant -> FC2 chains concurrently, so each chain's launch tail is
-// filled with the other's work. Default stream priority. The mutex keeps each
+// A second stream and three events per device, created on first use and kept
+// until the process ends: the two parts of the experts run their FC1 ->
+// requant -> FC2 chains concurrently, so each chain's launch tail is filled
+// with the other's work, and the one-call forward quantizes its input there
+// while the routing runs. Default stream priority. The mutex keeps each
 // call's record / wait pairs together when several host threads enqueue on
 // the same device.
 struct Aux {
   hipStream_t s2 = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, routed = nullptr;
 };
 std::mutex g_aux_mu;
 Aux g_aux[64];
 
 // The current device's Aux, created on first use. Call with g_aux_mu held.
-// Either all three objects exist afterwards or none is kept (a failed
+// Either all four objects exist afterwards or none is kept (a failed
 // creation is reported and retried on the next call).
 int aux_for_current_device(Aux** out) {
   int dev = 0;
@@ -342,7 +343,9 @@ int aux_for_current_device(Aux** out) {
     hipError_t e = hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.routed, hipEventDisableTiming);
     if (e != hipSuccess) {
+      if (n.routed) (void)hipEventDestroy(n.routed);
       if (n.join) (void)hipEventDestroy(n.join);
       if (n.fork) (void)hipEventDestroy(n.fork);
       if (n.s2) (void)hipStreamDestroy(n.s2);
@@ -417,26 +420,47 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   rb.row_of_route = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROW_OF_ROUTE]);
   rb.route_of_row = reinterpret_cast<int*>(base + L.off[PMOE_WS_ROUTE_OF_ROW]);
   auto run = [&](int step) { return first <= step && step <= last; };
-  if (bf16_input && rc != kW4A16) {
+  float* acc32 = reinterpret_cast<float*>(base + L.acc32);
+  const bool fill_acc = fused && run(PMOE_STEP_FC2);
+  const bool quant_in = bf16_input && rc != kW4A16;
+  // Two streams for the whole FC1..FC2 range when asked (streams == 2) or by
+  // default (streams == 0) once there is enough work to fill the GPU twice.
+  const bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
+                     (streams == 2 || (streams == 0 && TK >= 2048));
+  // One lock for the whole enqueue when the second stream is used, so that the
+  // record / wait pairs of concurrent host threads do not interleave.
+  std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
+  Aux* aux = nullptr;
+  if (quant_in || split) {
+    lock.lock();
+    PMOE_TRY(aux_for_current_device(&aux));
+  }
+  bool s2_after_route = false;  // the second stream already follows the routing
+  if (quant_in) {
     // quantize the BF16 activations on the second stream while routing runs
-    // on the caller's; both are joined before FC1
+    // on the caller's; each stream then waits for the other's part
     uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
     uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
     float* wsc = reinterpret_cast<float*>(base + L.x_scale);
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    Aux* aux = nullptr;
-    PMOE_TRY(aux_for_current_device(&aux));
     PMOE_HIP(hipEventRecord(aux->fork, s));
     PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
     PMOE_HIP(launch_quantize_bf16(x, T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, aux->s2));
     PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+    if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+    if (split) {
+      PMOE_HIP(hipEventRecord(aux->routed, s));
+      PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->routed, 0));
+      s2_after_route = true;
+    }
     PMOE_HIP(hipEventRecord(aux->join, aux->s2));
     PMOE_HIP(hipStreamWaitEvent(s, aux->join, 0));
     x = wq;
     x_sf = wsf;
     x_scale = rc == kPerToken ? wsc : nullptr;
-  } else if (run(PMOE_STEP_ROUTE)) {
-    PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+  } else {
+    if (run(PMOE_STEP_ROUTE))
+      PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
+    if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
   }
 
   void* h = base + L.off[PMOE_WS_H];  // FP32 h, or BF16 h under W4A16
@@ -483,7 +507,6 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p2.KC = I / kChunk;
   p2.out = z;
   p2.out_stride = H;
-  float* acc32 = reinterpret_cast<float*>(base + L.acc32);
   if (fused) {
     p2.out = acc32;
     p2.out_route = rb.route_of_row;
@@ -506,17 +529,11 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     if (fc2) PMOE_HIP(launch_fc(m2, q2, st));
     return PMOE_OK;
   };
-  if (fused && run(PMOE_STEP_FC2)) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
-  // Two streams for the whole FC1..FC2 range when asked (streams == 2) or by
-  // default (streams == 0) once there is enough work to fill the GPU twice.
-  const bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
-                     (streams == 2 || (streams == 0 && TK >= 2048));
   if (split) {
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    Aux* aux = nullptr;
-    PMOE_TRY(aux_for_current_device(&aux));
-    PMOE_HIP(hipEventRecord(aux->fork, s));
-    PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
+    if (!s2_after_route) {
+      PMOE_HIP(hipEventRecord(aux->fork, s));
+      PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
+    }
     PMOE_TRY(chain(1, s, true, true, true));
     PMOE_TRY(chain(2, aux->s2, true, true, true));
     PMOE_HIP(hipEventRecord(aux->join, aux->s2));

@@ -42,7 +42,7 @@ struct RouteBuffers {
   int* expert_offsets;  // [E+1]
   int* tiles;           // [max_tiles][4]: every M-tile of expert e holds {e, e's first row,
                         // e's first tile, e's row count}; tiles are grouped by expert
-  int* counters;        // [4] = {R, tiles, tiles of experts < ceil(E/2), rows of those experts}
+  int* counters;        // [4] = {R, tiles, first tile and first row of the second part}
   int* row_of_route;    // [TK]
   int* route_of_row;    // [TK]
 };
@@ -68,7 +68,7 @@ struct FcParams {
   int KC;                    // chunks of 64 along the reduction
   const int* tiles;          // [tiles][4], see RouteBuffers
   const int* expert_offsets;
-  const int* counters;       // [1] = number of M-tiles, [2] = M-tiles of the first expert half
+  const int* counters;       // [1] = number of M-tiles, [2] = first M-tile of the second part
   int part;                  // 0: all experts; 1 / 2: first / second half of the experts
   int max_tiles;
   void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z;

@@ -13,10 +13,10 @@
 //                   (in place), totals, exclusive scan over experts, the
 //                   M-tile list (tiles of 64 rows, grouped by expert in
 //                   expert order; every tile of an expert holds {expert, its
-//                   first row, its first tile, its row count}), and where the
-//                   first half of the
-//                   experts ends in tiles and rows (counters[2], counters[3]),
-//                   for running the two halves on two streams.
+//                   first row, its first tile, its row count}), and the
+//                   expert boundary nearest half of the tiles (counters[2],
+//                   counters[3]: first tile and row of the second part), for
+//                   running the two parts on two streams.
 //   route_scatter : row = expert start + block prefix + in-block rank;
 //                   writes row_of_route and route_of_row.
 // A route is valid iff expert_offset <= id < expert_offset + E; other ids
@@ -69,6 +69,29 @@ __global__ __launch_bounds__(256) void route_count_kernel(const IdT* __restrict_
 }
 
 // Inclusive block scan over 1024 threads (Hillis-Steele in LDS).
+#ifndef PMOE_SPLIT_PCT
+#define PMOE_SPLIT_PCT 50
+#endif
+// Where the expert-sorted tiles are cut into the two parts that run on two
+// streams: at the expert boundary nearest to PMOE_SPLIT_PCT % of the tiles
+// (counters[2] = first tile, counters[3] = first row of the second part).
+// The expert whose tiles straddle the target writes it; with no tiles at all,
+// the first thread writes 0.
+__device__ __forceinline__ void write_split(bool is_expert, int tstart, int ntiles, int start,
+                                            int rows, int total_tiles, bool first_thread,
+                                            int* counters) {
+  const int target = (int)((long long)total_tiles * PMOE_SPLIT_PCT / 100);
+  if (is_expert && ntiles > 0 && tstart <= target && target < tstart + ntiles) {
+    const bool before = target - tstart <= tstart + ntiles - target;
+    counters[2] = before ? tstart : tstart + ntiles;
+    counters[3] = before ? start : start + rows;
+  }
+  if (total_tiles == 0 && first_thread) {
+    counters[2] = 0;
+    counters[3] = 0;
+  }
+}
+
 // Inclusive prefix sum over the 1024 threads of a workgroup; the total is left
 // in sh[1023]. Each wave scans its 64 values with shuffles, then adds the
 // totals of the waves before it (two barriers instead of twenty).
@@ -135,10 +158,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int* __restrict__ bloc
     counters[0] = R;
     counters[1] = sh[1023];
   }
-  if (e == (E + 1) / 2) {  // the first expert of the second half (E itself when E == 1)
-    counters[2] = tstart;
-    counters[3] = start;
-  }
+  write_split(e < E, tstart, ntiles, start, total, sh[1023], e == 0, counters);
 }
 
 template <typename IdT>
@@ -225,10 +245,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     counters[0] = R;
     counters[1] = T_tiles;
   }
-  if (tid == (E + 1) / 2) {  // the first expert of the second half (E itself when E == 1)
-    counters[2] = tstart;
-    counters[3] = start;
-  }
+  write_split(tid < E, tstart, ntiles, start, total, T_tiles, tid == 0, counters);
 #pragma unroll
   for (int i = 0; i < kRouteSmallPer; ++i) {
     if (i * 1024 >= TK) break;  // uniform across the workgroup
