@@ -144,8 +144,6 @@ __device__ __forceinline__ void decode_scales4(uint32_t s, half2_t& s01, half2_t
   s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
 }
 
-// One dword of 8 E2M1 codes (element i in nibble i) times the block scale
-// `sc` -> 8 FP16 values in element order.
 // Eight E2M1 codes (low nibble first) times an FP32 block scale, as BF16. The
 // codes convert exactly to FP32, the product with an E4M3 scale has at most 6
 // significant bits and is exact in FP32, and its low 16 bits are zero, so
@@ -167,6 +165,8 @@ __device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t w, float sc) {
   return r;
 }
 
+// One dword of 8 E2M1 codes (element i in nibble i) times the block scale
+// `sc` -> 8 FP16 values in element order.
 __device__ __forceinline__ half8_t decode8(uint32_t w, _Float16 sc) {
   const half2_t s2 = {sc, sc};
   half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
