@@ -1,7 +1,9 @@
-"""GPU parity at the largest supported sizes: rows of 16384 elements for both
-quantizers (bit-exact), and the routed path with the longest reduction
-(H = 16384) and the widest FC1 (SwiGLU with I = 16384, N1 = 32768) against
-the oracle, to the per-token tolerance (1e-2 of the token's max)."""
+"""GPU parity at the limits: rows of 16384 elements for both quantizers
+(bit-exact); the routed path with the longest reduction (H = 16384) and the
+widest FC1 (SwiGLU with I = 16384, N1 = 32768); and degenerate expert sets
+(one expert, two experts split over two streams, every route on one expert so
+that one stream's part is empty). End-to-end results against the oracle to
+the per-token tolerance (1e-2 of the token's max)."""
 import numpy as np
 import pytest
 
@@ -61,5 +63,48 @@ def test_moe_largest_dims(pm, H, I, act):
     res = om.routed_moe(xq, xs, xg, ids, wts, om.prepare_weights(w1, w2), act)
     got = bf16_to_f32(bf16_bits(out)).astype(np.float64)
     want = bf16_to_f32(res.out).astype(np.float64)
+    err = np.abs(got - want).max(axis=1)
+    assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
+
+
+def _moe_case(pm, rng, T, K, E, H, I, act, ids):
+    N1 = 2 * I if act == "swiglu" else I
+    w1 = synth._bf16_np(rng.standard_normal((E, N1, H)).astype(np.float32) * 0.02)
+    w2 = synth._bf16_np(rng.standard_normal((E, H, I)).astype(np.float32) * 0.02)
+    x = synth._bf16_np(rng.standard_normal((T, H)).astype(np.float32))
+    wts = rng.uniform(0.1, 1.0, (T, K)).astype(np.float32)
+    P = pm.prepare_weights(dev_bf16(w1), dev_bf16(w2))
+    return w1, w2, x, wts, P
+
+
+@pytest.mark.parametrize("case", ["one_expert", "two_experts_split", "all_on_one_of_16"])
+def test_expert_count_edges(pm, case):
+    """Degenerate expert sets, with and without the two-stream split: E = 1;
+    E = 2 split into one expert per stream; every route on one expert of 16, so
+    one of the two parts is empty. Bit-equal across stream counts, and equal to
+    the oracle to the per-token tolerance."""
+    import torch
+    rng = np.random.default_rng(len(case))
+    H, I, act = 256, 128, "swiglu"
+    if case == "one_expert":
+        T, K, E = 300, 1, 1
+        ids = np.zeros((T, K), np.int32)
+    elif case == "two_experts_split":
+        T, K, E = 1200, 2, 2
+        ids = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+        ids[::3] = ids[::3, ::-1]
+    else:
+        T, K, E = 4096, 1, 16
+        ids = np.full((T, K), 5, np.int32)
+    w1, w2, x, wts, P = _moe_case(pm, rng, T, K, E, H, I, act, ids)
+    outs = [pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P, streams=s) for s in (1, 2, 0)]
+    _sync()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    toks = np.arange(T) if T <= 300 else np.array([0, 1, 2, T // 2, T - 1])
+    xq, xs, xg = oq.quantize_input_per_token(x)
+    res = om.routed_moe(xq, xs, xg, ids, wts, om.prepare_weights(w1, w2), act, tokens=toks)
+    got = bf16_to_f32(bf16_bits(outs[0])[toks]).astype(np.float64)
+    want = bf16_to_f32(res.out[toks]).astype(np.float64)
     err = np.abs(got - want).max(axis=1)
     assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
