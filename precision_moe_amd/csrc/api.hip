@@ -484,7 +484,6 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p1.NB = N1 / kColBlock;
   p1.KC = H / kChunk;
   p1.tiles = rb.tiles;
-  p1.expert_offsets = rb.expert_offsets;
   p1.counters = rb.counters;
   p1.max_tiles = L.max_tiles;
   p1.out = h;

@@ -67,9 +67,8 @@ struct FcParams {
   int NB;                    // column blocks of 32 in this FC
   int KC;                    // chunks of 64 along the reduction
   const int* tiles;          // [tiles][4], see RouteBuffers
-  const int* expert_offsets;
   const int* counters;       // [1] = number of M-tiles, [2] = first M-tile of the second part
-  int part;                  // 0: all experts; 1 / 2: first / second half of the experts
+  int part;                  // 0: all tiles; 1 / 2: the tiles before / from counters[2]
   int max_tiles;
   void* out;                 // FC1: h [rows][out_stride] (float, BF16 when a_bf16); FC2: BF16 z;
                              // FC2 fused: float accumulator [T][out_stride]
