@@ -69,20 +69,38 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   const float alpha = 1.0f / w_scale;    // then 0
   if (p == 0 && threadIdx.x == 0) alpha_out[e] = fold_a ? 1.0f / (w_scale * *fold_a) : alpha;
 
-  const int nkb = Kd / kBlock;
-  // chunk c of column block p sits at slab ((e*NT + p/8)*KC + c)*8 + p%8
+  // Chunk c of column block p is one 1 KB code slab (+ 128 B of scales) at
+  // slab ((e*NT + p/8)*KC + c)*8 + p%8. Two chunks per round: thread t
+  // quantizes, of row t/8 of the column block, block (t%8)%4 of chunk
+  // c0 + (t%8)/4; the codes and scales go into LDS in slab order, then the
+  // two slabs are copied out with 16-byte stores (the prepared layout spreads
+  // a block's codes over lanes, so storing them directly would write each
+  // line several times over).
+  __shared__ uint32_t lcodes[2][256];
+  __shared__ uint32_t lscales[2][32];
   const long tile_base = ((long)e * (NBp / kColTileBlocks) + p / kColTileBlocks) * KC;
   const int pos = p % kColTileBlocks;
-  for (int idx = threadIdx.x; idx < kColBlock * nkb; idx += 256) {
-    const int col = idx / nkb, kb = idx - col * nkb;
-    int n;  // canonical row (only read when p < NB)
-    if (gated_I > 0)
-      n = ((p & 1) ? gated_I : 0) + kColBlock * (p >> 1) + col;
-    else
-      n = kColBlock * p + col;
+  const int tid = threadIdx.x;
+  const int col = tid >> 3;  // row of the column block (0..31)
+  const int bl = tid & 7;    // block of the round: chunk bl/4, block bl%4 of that chunk
+  int n;                     // canonical row (only read when p < NB)
+  if (gated_I > 0)
+    n = ((p & 1) ? gated_I : 0) + kColBlock * (p >> 1) + col;
+  else
+    n = kColBlock * p + col;
+  const int cs = bl >> 2, j = bl & 3;
+  // block j of a chunk is half jj of k-step s; its row sits in 16-column
+  // block h of the position. Lane 32*jj + col%16 holds elements 0..7, lane
+  // + 16 elements 8..15, each as word 2h + s of its 16 bytes; the scale is
+  // byte 2h + s of dword col%16 + 16*jj.
+  const int s = j >> 1, jj = j & 1, h = col >> 4, n16 = col & 15;
+  const int lane_lo = 32 * jj + n16;
+  for (int c0 = 0; c0 < KC; c0 += 2) {
+    const int c = c0 + cs;
     uint32_t lo = 0, hi = 0, sf = 0;
-    if (p < NB) {
-      const uint4* src = reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + kb * kBlock);
+    if (p < NB && c < KC) {
+      const uint4* src =
+          reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + (4 * c + j) * kBlock);
       uint4 u0 = src[0], u1 = src[1];
       uint32_t v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
       float x[16];
@@ -93,18 +111,24 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
       }
       sf = quant_block16(x, alpha, lo, hi);
     }
-    // block j of chunk c is half jj of k-step s; its row sits in 16-column
-    // block h of the position. Lane 32*jj + col%16 holds elements 0..7, lane
-    // + 16 elements 8..15, each as word 2h + s of its 16 bytes; the scale is
-    // byte 2h + s of dword col%16 + 16*jj.
-    const int c = kb >> 2, j = kb & 3;
-    const int s = j >> 1, jj = j & 1, h = col >> 4, n16 = col & 15;
-    const int lane_lo = 32 * jj + n16;
-    const long slab = (tile_base + c) * kColTileBlocks + pos;
-    uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + slab * 1024);
-    cdst[lane_lo * 4 + 2 * h + s] = lo;
-    cdst[(lane_lo + 16) * 4 + 2 * h + s] = hi;
-    scales[slab * 128 + (n16 + 16 * jj) * 4 + 2 * h + s] = (uint8_t)sf;
+    lcodes[cs][lane_lo * 4 + 2 * h + s] = lo;
+    lcodes[cs][(lane_lo + 16) * 4 + 2 * h + s] = hi;
+    reinterpret_cast<uint8_t*>(lscales[cs])[(n16 + 16 * jj) * 4 + 2 * h + s] = (uint8_t)sf;
+    __syncthreads();
+    if (tid < 128) {  // codes: two slabs of 64 lanes x 16 bytes
+      const int k = tid >> 6, l = tid & 63;
+      if (c0 + k < KC) {
+        const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
+        reinterpret_cast<uint4*>(codes + slab * 1024)[l] = reinterpret_cast<const uint4*>(lcodes[k])[l];
+      }
+    } else if (tid < 144) {  // scales: two slabs of 8 x 16 bytes
+      const int k = (tid - 128) >> 3, q = (tid - 128) & 7;
+      if (c0 + k < KC) {
+        const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
+        reinterpret_cast<uint4*>(scales + slab * 128)[q] = reinterpret_cast<const uint4*>(lscales[k])[q];
+      }
+    }
+    __syncthreads();
   }
 }
 
