@@ -111,6 +111,37 @@ def test_moe_relu2_sampled(pm):
     _assert_rows_close(run.out_bits()[toks], res_t.out[toks], "out")
 
 
+def test_fc1_accumulation_within_summation_bound(pm):
+    """The GPU's FP32 accumulation of FC1 stays within the worst-case error of any
+    summation order: |acc_gpu - acc_exact| <= gamma_K * sum_k |a_k b_k| with
+    gamma_K = K u / (1 - K u) (Higham), u = 2^-23 (twice the unit roundoff, for
+    the matrix core's internal rounding). relu2 workload, K = H = 4096, every row
+    of two experts: the FP32 h = fp32(y^2), y = fp32(acc * s), is compared with
+    the exact y^2 through that bound, plus the two FP32 roundings."""
+    w = synth.WORKLOADS["relu2"]
+    run = GpuRun(pm, w)
+    xq, xs, xg = oq.quantize_input_per_token(run.x)
+    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    rt = om.route(run.ids, w.E)
+    h_gpu = run.views["h"].cpu().numpy()
+    u = 2.0 ** -23
+    gamma = w.H * u / (1 - w.H * u)
+    for e in (0, 37):
+        rows = np.arange(rt.offsets[e], rt.offsets[e + 1])
+        tok = rt.route_of_row[rows] // w.K
+        A = oq.dequantize_blocks(xq[tok], xs[tok])            # exact decoded values, float64
+        w1q, w1sf, al1 = W.expert(e)[:3]
+        B = oq.dequantize_blocks(w1q, w1sf)
+        s = (xg[tok].astype(np.float32) * np.float32(al1)).astype(np.float64)[:, None]
+        y = (A @ B.T) * s                                      # exact up to float64 rounding
+        dy = gamma * (np.abs(A) @ np.abs(B).T) * s * (1 + 2.0 ** -20) + u * np.abs(y)
+        h = h_gpu[rows].astype(np.float64)
+        bound = (2 * np.abs(y) + dy) * dy + (np.abs(y) + dy) ** 2 * u
+        ok = np.where(y > 0, np.abs(h - y * y) <= bound, h <= dy * dy * (1 + u))
+        bad = np.argwhere(~ok)
+        assert bad.size == 0, f"expert {e}: {len(bad)} entries outside the bound, first {bad[:4].tolist()}"
+
+
 # ----------------------------------------------------------------------------- full size
 @pytest.mark.parametrize("name", ["ep4_t512", "ep4_t1024"])
 def test_moe_ep4_sampled(pm, name):
