@@ -134,7 +134,7 @@ def test_per_tensor_moe_small(pm, name):
     _assert_rows_close(bf16_bits(run.out), res.out, "out")
 
 
-@pytest.mark.parametrize("name", ["relu2", "ep4_t1024"])
+@pytest.mark.parametrize("name", ["relu2", "ep4_t1024", "large"])
 def test_per_tensor_moe_sampled(pm, name):
     import torch
     w = synth.WORKLOADS[name]
@@ -192,7 +192,7 @@ def test_w4a16_moe_small(pm, name):
     _assert_rows_close(bf16_bits(run.out), res.out, "out")
 
 
-@pytest.mark.parametrize("name", ["relu2", "ep4_t512", "ep4_t1024"])
+@pytest.mark.parametrize("name", ["relu2", "ep4_t512", "ep4_t1024", "large"])
 def test_w4a16_moe_sampled(pm, name):
     import torch
     w = synth.WORKLOADS[name]
