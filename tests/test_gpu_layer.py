@@ -313,3 +313,23 @@ def test_forward_edges(pm, recipe):
     full = pm.moe_forward(xd, dev(ids), dev(wts), P, a1=fa1, **kw)
     _sync()
     assert not bf16_bits(full)[3].any()            # a token without valid routes gets +0
+
+
+def test_forward_batch_invariance_across_stream_split(pm):
+    """A token alone (one stream, one M-tile per expert) gives the same BF16 bits as
+    inside the full ep4_t1024 batch (two streams, split expert set, hot experts
+    spanning many M-tiles)."""
+    import torch
+    w = synth.WORKLOADS["ep4_t1024"]
+    x = synth.activations(w)
+    ids, wts = synth.router(w)
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    full = pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P)
+    toks = [0, int(np.nonzero((ids == 0).any(axis=1))[0][0]), 700, w.T - 1]
+    alone = [pm.moe_forward(dev_bf16(x[t:t + 1]), dev(ids[t:t + 1]), dev(wts[t:t + 1]), P) for t in toks]
+    _sync()
+    fb = bf16_bits(full)
+    for t, a in zip(toks, alone):
+        assert np.array_equal(bf16_bits(a)[0], fb[t]), f"token {t}"
+    del P
+    torch.cuda.empty_cache()
