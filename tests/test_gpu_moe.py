@@ -245,3 +245,35 @@ def test_act_mismatch_is_rejected(pm):
     with _pt.raises(pm.PmoeError) as ei:
         pm.routed_moe(run.xq, run.xs, run.xg, run.ids_dev, dev(run.wts), run.P, act=pm.ACT_SWIGLU)
     assert ei.value.code == 3 or ei.value.code == 4
+
+
+def test_pointer_and_workspace_errors_leave_output_untouched(pm):
+    """Host validation on a GPU: a host, a misaligned and a null pointer are
+    PMOE_ERR_POINTER, a workspace one byte short is PMOE_ERR_WORKSPACE, and in
+    every case nothing was launched: the output keeps its previous contents."""
+    import torch
+    w = synth.WORKLOADS["tiny"]
+    run = GpuRun(pm, w)
+    ids, wts = run.ids_dev, dev(run.wts)
+    out = torch.full((w.T, w.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    before = out.clone()
+
+    def expect(code, **kw):
+        args = dict(xq=run.xq, x_sf=run.xs, x_scale=run.xg, ws=run.ws)
+        args.update(kw)
+        with pytest.raises(pm.PmoeError) as ei:
+            pm.routed_moe(args["xq"], args["x_sf"], args["x_scale"], ids, wts, run.P,
+                          workspace=args["ws"], out=out)
+        assert ei.value.code == code, (code, str(ei.value))
+
+    expect(2, xq=run.xq.cpu())                                         # host memory
+    raw = torch.empty(run.xq.numel() + 16, dtype=torch.uint8, device="cuda")
+    expect(2, xq=raw[4:4 + run.xq.numel()].view(run.xq.shape))         # not 16-byte aligned
+    expect(2, x_scale=None)                                            # null
+    need = pm.moe_workspace_bytes(w.T, w.K, w.E, w.H, w.I, run.P.act)
+    expect(5, ws=torch.empty(need - 1, dtype=torch.uint8, device="cuda"))
+    _sync()
+    assert torch.equal(out.view(torch.int16), before.view(torch.int16))
+    pm.routed_moe(run.xq, run.xs, run.xg, ids, wts, run.P, workspace=run.ws, out=out)
+    _sync()
+    assert torch.equal(out.view(torch.int16), run.out.view(torch.int16))  # and the same call succeeds
