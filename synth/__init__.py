@@ -83,6 +83,9 @@ WORKLOADS = {
                           hot_experts=(0, 48), hot_bias=2.0),
     "large": Workload("large", 4, 4096, 7168, 2048, 256, 8, "swiglu", "outliers", 0.005, 50.0,
                       logits="uniform"),
+    # the single-GPU shape of [Megatron-LM #8262 . Performance] (all 256 experts
+    # local, squared ReLU, top-8), at 512 tokens: a context point, not a test config
+    "dsv3_relu2_t512": Workload("dsv3_relu2_t512", 5, 512, 7168, 2048, 256, 8, "relu2"),
 }
 
 
