@@ -333,3 +333,27 @@ def test_forward_batch_invariance_across_stream_split(pm):
         assert np.array_equal(bf16_bits(a)[0], fb[t]), f"token {t}"
     del P
     torch.cuda.empty_cache()
+
+
+def test_forward_repeat_determinism_full_size(pm):
+    """Race check: the one-call forward at ep4_t1024 (two streams, forked
+    quantization) gives identical bits over repeated calls, with other work on
+    the same workspace in between (a fused-finalize call and a W4A16 call)."""
+    import torch
+    w = synth.WORKLOADS["ep4_t1024"]
+    x = dev_bf16(synth.activations(w))
+    ids, wts = (dev(a) for a in synth.router(w))
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    ws = torch.empty(pm.moe_workspace_bytes(w.T, w.K, w.E, w.H, w.I, P.act), dtype=torch.uint8,
+                     device="cuda")
+    ref = pm.moe_forward(x, ids, wts, P, workspace=ws).clone()
+    for i in range(4):
+        if i % 2:
+            pm.moe_forward(x, ids, wts, P, finalize="fused", workspace=ws)
+        else:
+            pm.moe_forward(x, ids, wts, P, recipe="w4a16", workspace=ws)
+        out = pm.moe_forward(x, ids, wts, P, workspace=ws)
+        _sync()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"repeat {i}"
+    del P, ws
+    torch.cuda.empty_cache()
