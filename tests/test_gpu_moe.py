@@ -44,7 +44,7 @@ def _assert_rows_close(got_bits, want_bits, what):
     return float(np.median(err / np.maximum(scale, 1e-30)))
 
 
-class GpuRun:
+class GpuCase:
     """Inputs on the GPU, the prepared weights, and one routed_moe run."""
 
     def __init__(self, pm, w, T=None, ids=None, wts=None, x=None, weights=None, offset=0, ids64=False):
@@ -81,7 +81,7 @@ def _oracle(w, x, ids, wts, tokens=None, experts=None, weights=None):
 @pytest.mark.parametrize("name", ["tiny", "swiglu"])
 def test_moe_matches_oracle_small(pm, name):
     w = synth.WORKLOADS[name]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     res = _oracle(w, run.x, run.ids, run.wts)
     R = res.routing.route_of_row.size
     v = run.views
@@ -100,7 +100,7 @@ def test_moe_matches_oracle_small(pm, name):
 def test_moe_relu2_sampled(pm):
     """relu2 workload (T=1024, H=4096, I=2048, E=64, top-6): rows of two experts and two tokens."""
     w = synth.WORKLOADS["relu2"]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     experts = [0, 37]
     res = _oracle(w, run.x, run.ids, run.wts, experts=experts)
     rows = np.nonzero(res.computed_rows)[0]
@@ -119,7 +119,7 @@ def test_fc1_accumulation_within_summation_bound(pm):
     of two experts: the FP32 h = fp32(y^2), y = fp32(acc * s), is compared with
     the exact y^2 through that bound, plus the two FP32 roundings."""
     w = synth.WORKLOADS["relu2"]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     xq, xs, xg = oq.quantize_input_per_token(run.x)
     W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
     rt = om.route(run.ids, w.E)
@@ -148,7 +148,7 @@ def test_moe_ep4_sampled(pm, name):
     """The EP4 one-GPU share (E=96, H=7168, I=3072, top-6, two hot experts)."""
     import torch
     w = synth.WORKLOADS[name]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     counts = np.diff(run.views["expert_offsets"].cpu().numpy())
     assert counts[0] > 5 * np.median(counts)                         # a hot expert spans many M-tiles
     experts = [0, 17]
@@ -167,10 +167,10 @@ def test_large_batch_invariance_and_refresh(pm):
     refresh with new weights tracks the oracle of the new weights."""
     import torch
     w = synth.WORKLOADS["large"]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     full = run.out_bits()
     for t in (0, 2047, 4095):
-        one = GpuRun(pm, w, T=1, x=run.x[t:t + 1], ids=run.ids[t:t + 1], wts=run.wts[t:t + 1], weights=run.P)
+        one = GpuCase(pm, w, T=1, x=run.x[t:t + 1], ids=run.ids[t:t + 1], wts=run.wts[t:t + 1], weights=run.P)
         assert np.array_equal(one.out_bits()[0], full[t]), f"token {t}"
     res = _oracle(w, run.x, run.ids, run.wts, experts=[5])
     rows = np.nonzero(res.computed_rows)[0]
@@ -179,7 +179,7 @@ def test_large_batch_invariance_and_refresh(pm):
     w2 = w.with_(weight_epoch=1)
     ptr = run.P.w1_codes.data_ptr()
     pm.prepare_weights(*synth.all_weights(w2, device="cuda"), out=run.P)
-    again = GpuRun(pm, w, x=run.x, ids=run.ids, wts=run.wts, weights=run.P)
+    again = GpuCase(pm, w, x=run.x, ids=run.ids, wts=run.wts, weights=run.P)
     assert run.P.w1_codes.data_ptr() == ptr
     assert not np.array_equal(again.out_bits(), full)
     res2 = _oracle(w2, run.x, run.ids, run.wts, experts=[5])
@@ -199,7 +199,7 @@ def test_batch_invariance_with_large_cotokens(pm):
     x = synth.activations(w, 1024)
     ids, wts = synth.router(w, 1024)
     P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
-    alone = GpuRun(pm, w, T=target, x=x[:target], ids=ids[:target], wts=wts[:target], weights=P).out_bits()
+    alone = GpuCase(pm, w, T=target, x=x[:target], ids=ids[:target], wts=wts[:target], weights=P).out_bits()
     xf = bf16_to_f32(x)
     for total in (193, 1024):
         xb = xf[:total].copy()
@@ -208,24 +208,24 @@ def test_batch_invariance_with_large_cotokens(pm):
         xb[:target] = x[:target]
         ib = ids[:total].copy()
         ib[target:] = ids[rng.integers(0, target, total - target)]       # same experts as the target
-        big = GpuRun(pm, w, T=total, x=xb, ids=ib, wts=wts[:total], weights=P).out_bits()
+        big = GpuCase(pm, w, T=total, x=xb, ids=ib, wts=wts[:total], weights=P).out_bits()
         assert np.array_equal(big[:target], alone), f"batch of {total}"
 
 
 def test_expert_offset_int64_and_repeat(pm):
     w = synth.WORKLOADS["tiny"]
-    base = GpuRun(pm, w)
-    again = GpuRun(pm, w, weights=base.P)
+    base = GpuCase(pm, w)
+    again = GpuCase(pm, w, weights=base.P)
     assert np.array_equal(base.out_bits(), again.out_bits())
     assert np.array_equal(bf16_bits(base.views["z"]), bf16_bits(again.views["z"]))
     ids_shift = base.ids + 40
     ids_shift[1, 0] = -1
     ids_shift[2, 1] = 39                     # another rank's expert
-    shifted = GpuRun(pm, w, ids=ids_shift, wts=base.wts, weights=base.P, offset=40, ids64=True)
+    shifted = GpuCase(pm, w, ids=ids_shift, wts=base.wts, weights=base.P, offset=40, ids64=True)
     ref = base.ids.copy()
     ref[1, 0] = -1
     ref[2, 1] = -1
-    masked = GpuRun(pm, w, ids=ref, wts=base.wts, weights=base.P)
+    masked = GpuCase(pm, w, ids=ref, wts=base.wts, weights=base.P)
     assert np.array_equal(shifted.out_bits(), masked.out_bits())
     res = _oracle(w, base.x, ref, base.wts)
     _assert_rows_close(masked.out_bits(), res.out, "out with invalid routes")
@@ -234,14 +234,14 @@ def test_expert_offset_int64_and_repeat(pm):
 def test_all_routes_invalid_gives_zero(pm):
     w = synth.WORKLOADS["tiny"]
     ids = np.full((5, 2), -1, np.int32)
-    run = GpuRun(pm, w, T=5, ids=ids, wts=np.ones((5, 2), np.float32))
+    run = GpuCase(pm, w, T=5, ids=ids, wts=np.ones((5, 2), np.float32))
     assert not run.out_bits().any()
 
 
 def test_act_mismatch_is_rejected(pm):
     import pytest as _pt
     w = synth.WORKLOADS["tiny"]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     with _pt.raises(pm.PmoeError) as ei:
         pm.routed_moe(run.xq, run.xs, run.xg, run.ids_dev, dev(run.wts), run.P, act=pm.ACT_SWIGLU)
     assert ei.value.code == 3 or ei.value.code == 4
@@ -253,7 +253,7 @@ def test_pointer_and_workspace_errors_leave_output_untouched(pm):
     every case nothing was launched: the output keeps its previous contents."""
     import torch
     w = synth.WORKLOADS["tiny"]
-    run = GpuRun(pm, w)
+    run = GpuCase(pm, w)
     ids, wts = run.ids_dev, dev(run.wts)
     out = torch.full((w.T, w.H), 3.0, dtype=torch.bfloat16, device="cuda")
     before = out.clone()
