@@ -370,9 +370,10 @@ int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float* x_scale,
 /*
  * The whole routed layer from BF16 activations: for the NVFP4 recipes the
  * input is quantized inside the call (per token, or with options->a1_scale for
- * the per-tensor recipe) on the library's second stream while the routing runs
- * on the caller's stream, into the workspace; then the path of
- * pmoe_routed_moe_ex. For PMOE_RECIPE_W4A16 it is pmoe_routed_moe_ex on x.
+ * the per-tensor recipe) into the workspace: up to T*K = 8192 routes in the
+ * same launch as the routing, on the caller's stream; above that on the
+ * library's second stream while the routing runs on the caller's. Then the
+ * path of pmoe_routed_moe_ex. For PMOE_RECIPE_W4A16 it is pmoe_routed_moe_ex on x.
  *   x : BF16 [T, H]. Other arguments, options and errors as pmoe_routed_moe_ex
  *   (options == NULL: per-token, ordered, no clamp). The bits of the result
  *   equal quantize + pmoe_routed_moe(_ex) on the same inputs.

@@ -320,7 +320,9 @@ enum Recipe { kPerToken = PMOE_RECIPE_PER_TOKEN, kPerTensor = PMOE_RECIPE_PER_TE
 // until the process ends: the two parts of the experts run their FC1 ->
 // requant -> FC2 chains concurrently, so each chain's launch tail is filled
 // with the other's work, and the one-call forward quantizes its input there
-// while the routing runs. Default stream priority. The mutex keeps each
+// while the routing runs when the routing needs more than one workgroup
+// (otherwise both share one launch on the caller's stream). Default stream
+// priority. The mutex keeps each
 // call's record / wait pairs together when several host threads enqueue on
 // the same device.
 struct Aux {
@@ -431,12 +433,24 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   // record / wait pairs of concurrent host threads do not interleave.
   std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
   Aux* aux = nullptr;
-  if (quant_in || split) {
+  if ((quant_in && !route_quantize_fits(TK)) || split) {
     lock.lock();
     PMOE_TRY(aux_for_current_device(&aux));
   }
   bool s2_after_route = false;  // the second stream already follows the routing
-  if (quant_in) {
+  if (quant_in && route_quantize_fits(TK)) {
+    // route and quantize the BF16 activations in one launch on the caller's
+    // stream: FC1 can follow on the same stream with no cross-stream wait
+    uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
+    uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
+    float* wsc = reinterpret_cast<float*>(base + L.x_scale);
+    PMOE_HIP(launch_route_quantize(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, x,
+                                   T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, s));
+    if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+    x = wq;
+    x_sf = wsf;
+    x_scale = rc == kPerToken ? wsc : nullptr;
+  } else if (quant_in) {
     // quantize the BF16 activations on the second stream while routing runs
     // on the caller's; each stream then waits for the other's part
     uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);

@@ -49,6 +49,14 @@ struct RouteBuffers {
 int route_blocks(int TK);
 hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_offset,
                         const RouteBuffers& b, hipStream_t s);
+// The routing and the per-token (or static-scale) quantization of BF16 input
+// rows [T][H] in one launch, for TK routes that one workgroup can route
+// (route_quantize_fits); same results as launch_route + launch_quantize_bf16.
+bool route_quantize_fits(int TK);
+hipError_t launch_route_quantize(const void* ids, bool ids64, int TK, int E, int expert_offset,
+                                 const RouteBuffers& b, const void* x, int T, int H,
+                                 const float* static_a, uint8_t* xq, uint8_t* x_sf, float* x_scale,
+                                 hipStream_t s);
 
 // ---------------------------------------------------------------- grouped GEMMs
 enum FcMode { kFc1Relu2 = 0, kFc1Swiglu = 1, kFc2 = 2, kFc2Fused = 3 };

@@ -21,8 +21,7 @@
 //                   writes row_of_route and route_of_row.
 // A route is valid iff expert_offset <= id < expert_offset + E; other ids
 // (the -1 fill of unused slots, other ranks' experts) are skipped.
-#include "device.h"
-#include "kernels.h"
+#include "rowquant.h"
 
 namespace pmoe {
 
@@ -192,14 +191,24 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
 constexpr int kRouteSmall = 8192;
 constexpr int kRouteSmallPer = kRouteSmall / 1024;
 
+// LDS of the one-workgroup routing.
+struct RouteSmallLds {
+  int base[kMaxExperts];      // counts, then each expert's next free row
+  int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk (kept at 0)
+  int sh[1024];
+};
+
+// The routing body; the caller is a workgroup of 1024 threads.
 template <typename IdT>
-__global__ __launch_bounds__(1024) void route_small_kernel(
-    const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
-    int* __restrict__ expert_offsets, int* __restrict__ tiles, int* __restrict__ counters,
-    int* __restrict__ row_of_route, int* __restrict__ route_of_row) {
-  __shared__ int base[kMaxExperts];      // counts, then each expert's next free row
-  __shared__ int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk (kept at 0)
-  __shared__ int sh[1024];
+__device__ __forceinline__ void route_small_body(const IdT* __restrict__ ids, int TK, int E,
+                                                 int offset, int nbits,
+                                                 int* __restrict__ expert_offsets,
+                                                 int* __restrict__ tiles, int* __restrict__ counters,
+                                                 int* __restrict__ row_of_route,
+                                                 int* __restrict__ route_of_row, RouteSmallLds& lds) {
+  int* base = lds.base;
+  int(*wcnt)[kMaxExperts] = lds.wcnt;
+  int* sh = lds.sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int ev[kRouteSmallPer], rank[kRouteSmallPer], cnt[kRouteSmallPer];
 #pragma unroll
@@ -271,11 +280,82 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   }
 }
 
+template <typename IdT>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
+    int* __restrict__ expert_offsets, int* __restrict__ tiles, int* __restrict__ counters,
+    int* __restrict__ row_of_route, int* __restrict__ route_of_row) {
+  __shared__ RouteSmallLds lds;
+  route_small_body<IdT>(ids, TK, E, offset, nbits, expert_offsets, tiles, counters, row_of_route,
+                        route_of_row, lds);
+}
+
+// The routing and the per-token quantization of the BF16 input in one launch:
+// workgroup 0 routes (as route_small_kernel), workgroup b >= 1 quantizes rows
+// 4(b-1) .. 4(b-1)+3, one group of 256 threads per row (as
+// quantize_rows_kernel). The two jobs share no data, so they run side by side
+// and the grouped GEMM that needs both can follow on the same stream.
+template <typename IdT, bool kStatic>
+__global__ __launch_bounds__(1024) void route_quantize_kernel(
+    const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
+    int* __restrict__ expert_offsets, int* __restrict__ tiles, int* __restrict__ counters,
+    int* __restrict__ row_of_route, int* __restrict__ route_of_row, const void* __restrict__ x,
+    int T, int H, const float* __restrict__ static_a, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ x_sf, float* __restrict__ x_scale) {
+  __shared__ RouteSmallLds lds;
+  if (blockIdx.x == 0) {
+    route_small_body<IdT>(ids, TK, E, offset, nbits, expert_offsets, tiles, counters, row_of_route,
+                          route_of_row, lds);
+    return;
+  }
+  const int grp = threadIdx.x >> 8;
+  const long row = (long)(blockIdx.x - 1) * 4 + grp;
+  quantize_row<true, kStatic>(x, row, row < T, H, threadIdx.x & 255, static_a, xq, x_sf, x_scale,
+                              reinterpret_cast<float*>(lds.sh) + 4 * grp);
+}
+
+static int expert_bits(int E) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
+bool route_quantize_fits(int TK) { return TK <= kRouteSmall; }
+
+template <typename IdT>
+static void launch_route_quantize_t(const IdT* ids, int TK, int E, int expert_offset,
+                                    const RouteBuffers& b, const void* x, int T, int H,
+                                    const float* static_a, uint8_t* xq, uint8_t* x_sf,
+                                    float* x_scale, hipStream_t s) {
+  const int grid = 1 + (T + 3) / 4;
+  if (static_a)
+    route_quantize_kernel<IdT, true><<<grid, 1024, 0, s>>>(
+        ids, TK, E, expert_offset, expert_bits(E), b.expert_offsets, b.tiles, b.counters,
+        b.row_of_route, b.route_of_row, x, T, H, static_a, xq, x_sf, nullptr);
+  else
+    route_quantize_kernel<IdT, false><<<grid, 1024, 0, s>>>(
+        ids, TK, E, expert_offset, expert_bits(E), b.expert_offsets, b.tiles, b.counters,
+        b.row_of_route, b.route_of_row, x, T, H, nullptr, xq, x_sf, x_scale);
+}
+
+hipError_t launch_route_quantize(const void* ids, bool ids64, int TK, int E, int expert_offset,
+                                 const RouteBuffers& b, const void* x, int T, int H,
+                                 const float* static_a, uint8_t* xq, uint8_t* x_sf, float* x_scale,
+                                 hipStream_t s) {
+  if (!route_quantize_fits(TK)) return hipErrorInvalidValue;
+  if (ids64)
+    launch_route_quantize_t(static_cast<const long long*>(ids), TK, E, expert_offset, b, x, T, H,
+                            static_a, xq, x_sf, x_scale, s);
+  else
+    launch_route_quantize_t(static_cast<const int*>(ids), TK, E, expert_offset, b, x, T, H,
+                            static_a, xq, x_sf, x_scale, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_offset,
                         const RouteBuffers& b, hipStream_t s) {
   const int NB = route_blocks(TK);
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
+  const int nbits = expert_bits(E);
   if (TK <= kRouteSmall) {
     if (ids64)
       route_small_kernel<long long><<<1, 1024, 0, s>>>(

@@ -1,5 +1,5 @@
-"""Graph capture: the one-call forward (quantize on the library's second stream
-while routing runs, the two expert halves on two streams, the finalize),
+"""Graph capture: the one-call forward (routing and input quantization in one
+launch, the two expert halves on two streams, the finalize),
 captured in a HIP graph through torch.cuda.graph, replays to the eager result
 several times, with eager work and synchronizations between the replays
 (workspace and output overwritten in between): bit for bit with the ordered

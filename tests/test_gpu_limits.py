@@ -108,3 +108,25 @@ def test_expert_count_edges(pm, case):
     want = bf16_to_f32(res.out[toks]).astype(np.float64)
     err = np.abs(got - want).max(axis=1)
     assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
+
+
+@pytest.mark.parametrize("T", [2048, 2049])
+def test_forward_route_quantize_boundary(pm, T):
+    """The one-call forward routes and quantizes its BF16 input in one launch
+    up to 8192 routes (T = 2048, K = 4) and in separate launches on two streams
+    above (T = 2049): both give the bits of the separate quantize call followed
+    by pmoe_routed_moe, with int32 and int64 ids."""
+    import torch
+    rng = np.random.default_rng(T)
+    K, E, H, I = 4, 16, 256, 128
+    ids = np.argsort(rng.standard_normal((T, E)), axis=1)[:, :K].astype(np.int32)
+    ids[7] = -1                                          # a token without routes
+    w1, w2, x, wts, P = _moe_case(pm, rng, T, K, E, H, I, "swiglu", ids)
+    xd = dev_bf16(x)
+    xq, xs, xg = pm.quantize_input_per_token(xd)
+    ref = pm.routed_moe(xq, xs, xg, dev(ids), dev(wts), P)
+    for idt in (np.int32, np.int64):
+        got = pm.moe_forward(xd, dev(ids.astype(idt)), dev(wts), P)
+        _sync()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), idt
+    assert not bf16_bits(ref)[7].any()
