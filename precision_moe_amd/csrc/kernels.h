@@ -15,8 +15,7 @@ __host__ __device__ inline int padded_col_blocks(int NB) {
 }
 constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxBlocksPerThread = 4;  // per-row quantizer: rows up to 256*4*16 = 16384 elements
-constexpr int kMaxRow = 256 * kMaxBlocksPerThread * 16;
+constexpr int kMaxRow = 16384;  // longest row (H, I) the path accepts
 
 // ---------------------------------------------------------------- quantizers
 // static_a: null for per-row scales (written to *_scale), else the device

@@ -179,22 +179,27 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
 }
 
 // The whole routing in one workgroup of 1024 threads, for up to
-// kRouteSmall routes (one launch instead of three). Each thread loads all of
-// its ids up front (one memory latency, not one per chunk). Routes are taken
-// in chunks of 1024 in route order; within a wave, lanes with the same expert
-// find each other by ballots on the expert id bits, which gives each route its
-// rank among them and one leader per (wave, expert) that adds the group's size
-// to the expert's count (few LDS atomics even on a hot expert). A route's row
-// is then its expert's start + the rows its expert got in earlier chunks + in
-// earlier waves of this chunk + its rank: the same stable order as the
-// three-kernel path.
+// kRouteSmall routes (one launch instead of three). Wave w owns the
+// contiguous routes [w*seg*64, (w+1)*seg*64) (seg = ceil(TK / 1024) chunks of
+// 64) and loads all of its ids up front. Within a chunk, lanes with the same
+// expert find each other by ballots on the expert id bits, which gives each
+// route its rank among them and one leader per (chunk, expert) that adds the
+// group's size to the wave's own count of that expert in LDS; each route
+// first reads that count (its expert's routes in the wave's earlier chunks).
+// Only the wave itself touches its counts and a wave's LDS operations run in
+// program order, so the chunks need no barrier. After one barrier, each
+// expert's counts become exclusive prefixes over the waves and its total
+// feeds the scans. A route's row is then its expert's start + the expert's
+// routes in earlier waves + in the wave's earlier chunks + its rank: the same
+// stable order (ascending route index within an expert) as the three-kernel
+// path.
 constexpr int kRouteSmall = 8192;
 constexpr int kRouteSmallPer = kRouteSmall / 1024;
 
 // LDS of the one-workgroup routing.
 struct RouteSmallLds {
-  int base[kMaxExperts];      // counts, then each expert's next free row
-  int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk (kept at 0)
+  int base[kMaxExperts];      // each expert's first row
+  int wcnt[16][kMaxExperts];  // routes per (wave, expert), then the exclusive prefix over waves
   int sh[1024];
 };
 
@@ -210,31 +215,48 @@ __device__ __forceinline__ void route_small_body(const IdT* __restrict__ ids, in
   int(*wcnt)[kMaxExperts] = lds.wcnt;
   int* sh = lds.sh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int ev[kRouteSmallPer], rank[kRouteSmallPer], cnt[kRouteSmallPer];
+  const int seg = (TK + 1023) >> 10;  // chunks of 64 per wave, at most kRouteSmallPer
+  const int f0 = wave * seg * 64 + lane;
+  int ev[kRouteSmallPer], rank[kRouteSmallPer], before[kRouteSmallPer];
 #pragma unroll
-  for (int i = 0; i < kRouteSmallPer; ++i) {
-    const int f = i * 1024 + tid;
-    ev[i] = f < TK ? local_expert(ids, f, E, offset) : -1;
+  for (int c = 0; c < kRouteSmallPer; ++c) {
+    const int f = f0 + 64 * c;
+    ev[c] = (c < seg && f < TK) ? local_expert(ids, f, E, offset) : -1;
   }
-  for (int i = tid; i < kMaxExperts; i += 1024) base[i] = 0;
   for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int* mine = wcnt[wave];
 #pragma unroll
-  for (int i = 0; i < kRouteSmallPer; ++i) {
-    const int e = ev[i];
+  for (int c = 0; c < kRouteSmallPer; ++c) {
+    rank[c] = 0;
+    before[c] = 0;
+    if (c >= seg) continue;  // uniform across the workgroup
+    const int e = ev[c];
     uint64_t match = __ballot(e >= 0);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
       const uint64_t set = __ballot(bit);
       match &= bit ? set : ~set;
     }
-    rank[i] = __popcll(match & below);
-    cnt[i] = __popcll(match);
-    if (e >= 0 && rank[i] == 0) atomicAdd(&base[e], cnt[i]);
+    rank[c] = __popcll(match & below);
+    if (e >= 0) {
+      before[c] = mine[e];  // read before this chunk's leaders add to it
+      if (rank[c] == 0) atomicAdd(&mine[e], __popcll(match));
+    }
   }
   __syncthreads();
-  const int total = tid < E ? base[tid] : 0;
+  int total = 0;
+  if (tid < E) {
+    int cw[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) cw[w] = wcnt[w][tid];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      wcnt[w][tid] = total;
+      total += cw[w];
+    }
+  }
   const int incl = block_inclusive_scan_1024(total, sh);
   const int start = incl - total;
   const int R = sh[1023];
@@ -255,28 +277,19 @@ __device__ __forceinline__ void route_small_body(const IdT* __restrict__ ids, in
     counters[1] = T_tiles;
   }
   write_split(tid < E, tstart, ntiles, start, total, T_tiles, tid == 0, counters);
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRouteSmallPer; ++i) {
-    if (i * 1024 >= TK) break;  // uniform across the workgroup
-    const int f = i * 1024 + tid;
-    const int e = ev[i];
-    const bool lead = e >= 0 && rank[i] == 0;
-    if (lead) wcnt[wave][e] = cnt[i];
-    __syncthreads();  // (also orders the first chunk after base = start)
+  for (int c = 0; c < kRouteSmallPer; ++c) {
+    if (c >= seg) break;  // uniform
+    const int f = f0 + 64 * c;
+    const int e = ev[c];
     if (e >= 0) {
-      int row = base[e] + rank[i];
-      for (int w = 0; w < wave; ++w) row += wcnt[w][e];
+      const int row = base[e] + mine[e] + before[c] + rank[c];
       row_of_route[f] = row;
       route_of_row[row] = f;
     } else if (f < TK) {
       row_of_route[f] = -1;
     }
-    __syncthreads();
-    if (lead) {
-      atomicAdd(&base[e], cnt[i]);
-      wcnt[wave][e] = 0;
-    }
-    __syncthreads();
   }
 }
 
@@ -292,9 +305,10 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 
 // The routing and the per-token quantization of the BF16 input in one launch:
 // workgroup 0 routes (as route_small_kernel), workgroup b >= 1 quantizes rows
-// 4(b-1) .. 4(b-1)+3, one group of 256 threads per row (as
-// quantize_rows_kernel). The two jobs share no data, so they run side by side
-// and the grouped GEMM that needs both can follow on the same stream.
+// 4(b-1) .. 4(b-1)+3, one group of 256 threads per row (quantize_row_group:
+// the same bytes as quantize_rows_kernel). The two jobs share no data, so
+// they run side by side and the grouped GEMM that needs both can follow on
+// the same stream.
 template <typename IdT, bool kStatic>
 __global__ __launch_bounds__(1024) void route_quantize_kernel(
     const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
@@ -310,8 +324,8 @@ __global__ __launch_bounds__(1024) void route_quantize_kernel(
   }
   const int grp = threadIdx.x >> 8;
   const long row = (long)(blockIdx.x - 1) * 4 + grp;
-  quantize_row<true, kStatic>(x, row, row < T, H, threadIdx.x & 255, static_a, xq, x_sf, x_scale,
-                              reinterpret_cast<float*>(lds.sh) + 4 * grp);
+  quantize_row_group<true, kStatic>(x, row, row < T, H, threadIdx.x & 255, static_a, xq, x_sf,
+                                    x_scale, reinterpret_cast<float*>(lds.sh) + 4 * grp);
 }
 
 static int expert_bits(int E) {

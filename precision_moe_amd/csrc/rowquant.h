@@ -1,15 +1,18 @@
-// One row of the per-row NVFP4 quantizer, done by a group of 256 threads:
-// the per-token activation quantizer (BF16 rows) and the requantizer of the
-// FP32 expert intermediate (FP32 rows) [Megatron-LM #8262 . Background; What
-// is added; How to extend]. Shared by the standalone quantizer kernels and the
-// launch that routes and quantizes the input together.
+// One row of the per-row NVFP4 quantizer: the per-token activation quantizer
+// (BF16 rows) and the requantizer of the FP32 expert intermediate (FP32 rows)
+// [Megatron-LM #8262 . Background; What is added; How to extend].
 //
-// Thread lt of the group owns 16-element blocks lt, lt+256, ... (at most
-// kMaxBlocksPerThread), keeps them in registers, the group reduces the row's
-// absolute maximum (max is exact and order-free), then each thread quantizes
-// its blocks: g = fp32(amax * fp32(1/2688)), E4M3 block scales, E2M1 codes,
-// with the exact steps of quant_block16. With a static scale a (per-tensor
-// recipe) every row uses g = fp32(1 / a) instead and no scale is written.
+// The row's absolute maximum (exact and order-free), g = fp32(amax *
+// fp32(1/2688)), then per 16-element block the exact steps of quant_block16:
+// E4M3 block scale, E2M1 codes. With a static scale a (per-tensor recipe)
+// every row uses g = fp32(1 / a) instead and no scale is written.
+//
+// Two bodies, the same bytes: quantize_row (one wave per row, two passes),
+// used by the standalone quantizer kernels, whose looping grids then start
+// few waves -- starting waves is what bounds them while the grouped GEMMs
+// hold the GPU; and quantize_row_group (256 threads per row, one pass from
+// registers), used where the input is quantized beside the routing, where
+// more waves per row hide the load latency better.
 #pragma once
 
 #include "device.h"
@@ -42,23 +45,84 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
 }
 
 // Row `row` of x ([rows][L], BF16 or FP32) -> q [rows][L/2], sf [rows][L/16],
-// scale [rows] (per-row recipe). lt: the thread's index in its group of 256.
-// red: 4 floats of LDS owned by this group. Without a static scale the call
-// holds one workgroup barrier: every thread of the workgroup must make it the
-// same number of times, so a group with no row passes active = false (it
-// takes the barrier and touches no memory).
+// scale [rows] (per-row recipe), by one whole wave (lane = 0..63; every lane
+// of the wave calls it for the same row). Two passes over the row: lane l's
+// blocks are l, l+64, ...; pass 1 reads them for the row amax (a wave
+// reduction: no LDS, no barrier), pass 2 reads them again (from cache) and
+// quantizes four blocks at a time.
 template <bool kBf16, bool kStatic>
-__device__ __forceinline__ void quantize_row(const void* __restrict__ x, long row, bool active,
-                                             int L, int lt, const float* __restrict__ static_a,
-                                             uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
-                                             float* __restrict__ scale, float* red) {
+__device__ __forceinline__ void quantize_row(const void* __restrict__ x, long row, int L,
+                                                  int lane, const float* __restrict__ static_a,
+                                                  uint8_t* __restrict__ q,
+                                                  uint8_t* __restrict__ sf,
+                                                  float* __restrict__ scale) {
   const int nblk = L / kBlock;
   const void* xr = kBf16 ? (const void*)(static_cast<const uint16_t*>(x) + row * L)
                          : (const void*)(static_cast<const float*>(x) + row * L);
-  float v[kMaxBlocksPerThread][16];
+  constexpr int kGroup = 4;  // blocks in registers at once per lane
+  float g;
+  if constexpr (kStatic) {
+    g = 1.0f / *static_a;  // IEEE division (correctly rounded)
+  } else {
+    float amax = 0.0f;
+    for (int b0 = lane; b0 < nblk; b0 += 64 * kGroup) {
+      float v[kGroup][16];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i)
+        if (b0 + 64 * i < nblk) load_block16<kBf16>(xr, b0 + 64 * i, v[i]);
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i)
+        if (b0 + 64 * i < nblk) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][k]));
+        }
+    }
+    g = wave_max(amax) * kRecipeConst;
+  }
+  uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
+  uint8_t* sr = sf + row * nblk;
+  for (int b0 = lane; b0 < nblk; b0 += 64 * kGroup) {
+    float v[kGroup][16];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i)
+      if (b0 + 64 * i < nblk) load_block16<kBf16>(xr, b0 + 64 * i, v[i]);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const int b = b0 + 64 * i;
+      if (b < nblk) {
+        uint32_t lo, hi;
+        const uint32_t s = quant_block16(v[i], g, lo, hi);
+        qr[b] = make_uint2(lo, hi);
+        sr[b] = (uint8_t)s;
+      }
+    }
+  }
+  if constexpr (!kStatic) {
+    if (lane == 0) scale[row] = g;
+  }
+}
+
+
+// The same row with a group of 256 threads (lt = 0..255): thread lt owns
+// blocks lt, lt+256, ... (at most 4, rows up to 16384), kept in registers for
+// a single pass; the group's amax goes through `red` (4 floats of LDS owned by
+// the group) and one workgroup barrier, so every thread of the workgroup makes
+// the call, and a group with no row passes active = false.
+template <bool kBf16, bool kStatic>
+__device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, long row,
+                                                   bool active, int L, int lt,
+                                                   const float* __restrict__ static_a,
+                                                   uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ sf,
+                                                   float* __restrict__ scale, float* red) {
+  constexpr int kPer = kMaxRow / 16 / 256;
+  const int nblk = L / kBlock;
+  const void* xr = kBf16 ? (const void*)(static_cast<const uint16_t*>(x) + row * L)
+                         : (const void*)(static_cast<const float*>(x) + row * L);
+  float v[kPer][16];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxBlocksPerThread; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     const int b = lt + 256 * i;
     if (active && b < nblk) {
       load_block16<kBf16>(xr, b, v[i]);
@@ -70,7 +134,7 @@ __device__ __forceinline__ void quantize_row(const void* __restrict__ x, long ro
   }
   float g;
   if constexpr (kStatic) {
-    g = 1.0f / *static_a;  // IEEE division (correctly rounded)
+    g = 1.0f / *static_a;
   } else {
     amax = wave_max(amax);
     if ((lt & 63) == 0) red[lt >> 6] = amax;
@@ -82,7 +146,7 @@ __device__ __forceinline__ void quantize_row(const void* __restrict__ x, long ro
   uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
   uint8_t* sr = sf + row * nblk;
 #pragma unroll
-  for (int i = 0; i < kMaxBlocksPerThread; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     const int b = lt + 256 * i;
     if (b < nblk) {
       uint32_t lo, hi;
