@@ -292,7 +292,8 @@ PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, v
   PMOE_TRY(check_ptr(h_sf, 4, "h_sf"));
   PMOE_TRY(check_ptr(h_scale, 4, "h_scale"));
   PMOE_HIP(launch_quantize_f32(h, R, nullptr, nullptr, L, nullptr, static_cast<uint8_t*>(hq),
-                               static_cast<uint8_t*>(h_sf), h_scale, static_cast<hipStream_t>(stream)));
+                               static_cast<uint8_t*>(h_sf), h_scale, false,
+                               static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -538,7 +539,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     if (fc1) PMOE_HIP(launch_fc(m1, q1, st));
     if (requant && rc != kW4A16)
       PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, row_begin, row_end, I,
-                                   static_a2, hq, h_sf, h_scale, st));
+                                   static_a2, hq, h_sf, h_scale, part != 0, st));
     if (fc2) PMOE_HIP(launch_fc(m2, q2, st));
     return PMOE_OK;
   };

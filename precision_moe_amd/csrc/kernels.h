@@ -23,9 +23,11 @@ constexpr int kMaxRow = 16384;  // longest row (H, I) the path accepts
 hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
                                 uint8_t* x_sf, float* x_scale, hipStream_t s);
 // Rows [*row_begin_dev, *row_end_dev) of R (either pointer may be null: 0 / R).
+// beside_gemm: the launch runs while another stream's grouped GEMM holds the
+// CUs (one wave per row over a bounded grid); else one workgroup per row.
 hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
                                const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, hipStream_t s);
+                               uint8_t* h_sf, float* h_scale, bool beside_gemm, hipStream_t s);
 
 // ---------------------------------------------------------------- weights
 int weight_amax_parts(long elems);

@@ -6,19 +6,26 @@
 // extend]) every row uses g = fp32(1 / a) instead of its own amax, read from
 // device memory so that nothing waits on the host; no scale is written.
 //
-// One wave per row (the row body is quantize_row) and a bounded grid whose
-// waves loop over the rows. Loads and stores of a wave are contiguous spans.
-// Algorithmic bytes: a BF16 row of H elements moves 2H in and 9H/16 out; an
-// FP32 row 4L in and 9L/16 out.
+// Two kernels with the same bytes. quantize_rows_kernel gives each row a
+// workgroup of 256 threads (quantize_row_group: one pass from registers),
+// the faster layout when the quantizer has the GPU to itself.
+// quantize_rows_loop_kernel gives each row one wave (quantize_row) and loops a
+// bounded grid over the rows: it starts a few thousand waves instead of four
+// per row, which is what it costs while the other stream's grouped GEMM holds
+// the CUs (the requant of one expert half inside the two-stream path).
+// Loads and stores of a wave are contiguous spans. Algorithmic bytes: a BF16
+// row of H elements moves 2H in and 9H/16 out; an FP32 row 4L in and 9L/16
+// out.
 #include "rowquant.h"
 
 namespace pmoe {
 
 // Rows [begin, end): begin = *row_begin_dev (0 if null), end = *row_end_dev
 // (rows if null), read at run time (the intermediate has a device-side count
-// of valid routes). Wave w of workgroup b takes rows begin + 4b + w, then
-// every 4 * gridDim.x rows after it.
-// static_a: null for per-row scales, else the static scale a (kStatic).
+// of valid routes). static_a: null for per-row scales, else the static scale
+// a (kStatic).
+//
+// Workgroup b handles row begin + b (the grid covers every row that can exist).
 template <bool kBf16, bool kStatic>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int rows,
                                                             const int* __restrict__ row_begin_dev,
@@ -27,6 +34,20 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             float* __restrict__ scale) {
+  __shared__ float red[4];
+  const long row = blockIdx.x + (row_begin_dev ? *row_begin_dev : 0);
+  const int nrows = row_end_dev ? *row_end_dev : rows;
+  if (row >= nrows) return;  // uniform across the workgroup
+  quantize_row_group<kBf16, kStatic>(x, row, true, L, threadIdx.x, static_a, q, sf, scale, red);
+}
+
+// Wave w of workgroup b takes rows begin + 4b + w, then every 4 * gridDim.x
+// rows after it.
+template <bool kBf16, bool kStatic>
+__global__ __launch_bounds__(256) void quantize_rows_loop_kernel(
+    const void* __restrict__ x, int rows, const int* __restrict__ row_begin_dev,
+    const int* __restrict__ row_end_dev, int L, const float* __restrict__ static_a,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ sf, float* __restrict__ scale) {
   const long begin = row_begin_dev ? *row_begin_dev : 0;
   const long end = row_end_dev ? *row_end_dev : rows;
   const long step = (long)gridDim.x * 4;
@@ -34,34 +55,41 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
     quantize_row<kBf16, kStatic>(x, row, L, threadIdx.x & 63, static_a, q, sf, scale);
 }
 
-// Workgroups of four waves, one row per wave and pass, at most kQuantGroups
-// of them (rows beyond take further passes).
-constexpr int kQuantGroups = 512;
-static int quant_grid(int rows) {
+// At most kLoopGroups workgroups of four waves for the looping kernel.
+constexpr int kLoopGroups = 512;
+static int loop_grid(int rows) {
   const int g = (rows + 3) / 4;
-  return g < 1 ? 1 : (g < kQuantGroups ? g : kQuantGroups);
+  return g < 1 ? 1 : (g < kLoopGroups ? g : kLoopGroups);
 }
 
 hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
                                 uint8_t* x_sf, float* x_scale, hipStream_t s) {
   if (static_a)
-    quantize_rows_kernel<true, true><<<quant_grid(T), 256, 0, s>>>(x, T, nullptr, nullptr, H,
-                                                                   static_a, xq, x_sf, nullptr);
+    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, static_a, xq, x_sf,
+                                                       nullptr);
   else
-    quantize_rows_kernel<true, false><<<quant_grid(T), 256, 0, s>>>(x, T, nullptr, nullptr, H,
-                                                                    nullptr, xq, x_sf, x_scale);
+    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, nullptr, xq, x_sf,
+                                                        x_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
                                const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, hipStream_t s) {
-  if (static_a)
-    quantize_rows_kernel<false, true><<<quant_grid(R), 256, 0, s>>>(h, R, row_begin_dev, row_end_dev,
-                                                                    L, static_a, hq, h_sf, nullptr);
-  else
-    quantize_rows_kernel<false, false><<<quant_grid(R), 256, 0, s>>>(h, R, row_begin_dev, row_end_dev,
-                                                                     L, nullptr, hq, h_sf, h_scale);
+                               uint8_t* h_sf, float* h_scale, bool beside_gemm, hipStream_t s) {
+  if (beside_gemm) {
+    if (static_a)
+      quantize_rows_loop_kernel<false, true><<<loop_grid(R), 256, 0, s>>>(
+          h, R, row_begin_dev, row_end_dev, L, static_a, hq, h_sf, nullptr);
+    else
+      quantize_rows_loop_kernel<false, false><<<loop_grid(R), 256, 0, s>>>(
+          h, R, row_begin_dev, row_end_dev, L, nullptr, hq, h_sf, h_scale);
+  } else if (static_a) {
+    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, static_a,
+                                                        hq, h_sf, nullptr);
+  } else {
+    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, nullptr,
+                                                         hq, h_sf, h_scale);
+  }
   return hipGetLastError();
 }
 

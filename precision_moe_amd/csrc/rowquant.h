@@ -7,12 +7,12 @@
 // E4M3 block scale, E2M1 codes. With a static scale a (per-tensor recipe)
 // every row uses g = fp32(1 / a) instead and no scale is written.
 //
-// Two bodies, the same bytes: quantize_row (one wave per row, two passes),
-// used by the standalone quantizer kernels, whose looping grids then start
-// few waves -- starting waves is what bounds them while the grouped GEMMs
-// hold the GPU; and quantize_row_group (256 threads per row, one pass from
-// registers), used where the input is quantized beside the routing, where
-// more waves per row hide the load latency better.
+// Two bodies, the same bytes: quantize_row_group (256 threads per row, one
+// pass from registers: more waves per row hide the load latency), used where
+// the quantizer has the GPU to itself or shares it with the routing; and
+// quantize_row (one wave per row, two passes), used by a looping grid that
+// starts few waves -- starting waves is what bounds a quantizer launched
+// while another stream's grouped GEMM holds the CUs.
 #pragma once
 
 #include "device.h"
