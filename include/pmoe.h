@@ -331,7 +331,7 @@ typedef struct pmoe_moe_options {
   float swiglu_limit;     /* > 0: SwiGLU clamp, gate <= L and -L <= up <= L; 0: none         */
   const float* a2_scale;  /* per-tensor recipe: device float32 scalar; otherwise NULL       */
   int streams;            /* 0: automatic (two once T*K >= 2048); 1: one stream; 2: the
-                             experts are cut at the expert boundary nearest half of the
+                             experts are cut at the expert boundary nearest 44 % of the
                              M-tiles and the two parts run FC1 -> requant -> FC2 on the
                              caller's stream and on a second stream, joined before the
                              finalize (same bits either way; needs E >= 2)              */
