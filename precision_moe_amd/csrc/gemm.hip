@@ -30,7 +30,8 @@
 //     scales are already in the decoded values; FP32 accumulation.
 // Epilogue: y = acc * fp32(g_row * alpha_e) (scales applied after
 // accumulation, never folded into decoded values), then
-//   FC1 squared ReLU: h = max(y, 0)^2;  FC1 SwiGLU: h = silu(gate) * up (gate
+//   FC1 squared ReLU: h = max(y, 0)^2;  FC1 SwiGLU: h = silu(gate) * up, with
+//   silu(g) = g * rcp(1 + exp(-g)) on the hardware exp and reciprocal (gate
 //   and up column blocks of one output sit in the same wave), optionally with
 //   the clamp gate <= L, -L <= up <= L;  FC2: bf16(y);  FC2 with the fused
 //   finalize: FP32 atomic add of w * y into the token's row (order-free).
@@ -393,7 +394,9 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
                 g = __builtin_fminf(g, P.swiglu_limit);
                 u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
               }
-              const float silu = g / (1.0f + expf(-g));
+              // hardware exp and reciprocal (a few ulp; h is compared to
+              // tolerance, and the requant works on whatever h this writes)
+              const float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
               put(m - r_lo, lc, silu * u);
             } else {
               put(m - r_lo, lc, c0 * s);
