@@ -9,10 +9,11 @@
 // Two kernels with the same bytes. quantize_rows_kernel gives each row a
 // workgroup of 256 threads (quantize_row_group: one pass from registers),
 // the faster layout when the quantizer has the GPU to itself.
-// quantize_rows_loop_kernel gives each row one wave (quantize_row) and loops a
-// bounded grid over the rows: it starts a few thousand waves instead of four
-// per row, which is what it costs while the other stream's grouped GEMM holds
-// the CUs (the requant of one expert half inside the two-stream path).
+// quantize_rows_loop_kernel gives each row one wave (quantize_row_wave) and
+// loops a bounded grid over the rows: it starts a few thousand waves instead
+// of four per row, which is what it costs while the other stream's grouped
+// GEMM holds the CUs (the requant of one expert half inside the two-stream
+// path).
 // Loads and stores of a wave are contiguous spans. Algorithmic bytes: a BF16
 // row of H elements moves 2H in and 9H/16 out; an FP32 row 4L in and 9L/16
 // out.
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void quantize_rows_loop_kernel(
   const long end = row_end_dev ? *row_end_dev : rows;
   const long step = (long)gridDim.x * 4;
   for (long row = begin + (long)blockIdx.x * 4 + (threadIdx.x >> 6); row < end; row += step)
-    quantize_row<kBf16, kStatic>(x, row, L, threadIdx.x & 63, static_a, q, sf, scale);
+    quantize_row_wave<kBf16, kStatic>(x, row, L, threadIdx.x & 63, static_a, q, sf, scale);
 }
 
 // At most kLoopGroups workgroups of four waves for the looping kernel.

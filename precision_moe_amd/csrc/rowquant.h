@@ -10,7 +10,7 @@
 // Two bodies, the same bytes: quantize_row_group (256 threads per row, one
 // pass from registers: more waves per row hide the load latency), used where
 // the quantizer has the GPU to itself or shares it with the routing; and
-// quantize_row (one wave per row, two passes), used by a looping grid that
+// quantize_row_wave (one wave per row, two passes), used by a looping grid that
 // starts few waves -- starting waves is what bounds a quantizer launched
 // while another stream's grouped GEMM holds the CUs.
 #pragma once
@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
 // reduction: no LDS, no barrier), pass 2 reads them again (from cache) and
 // quantizes four blocks at a time.
 template <bool kBf16, bool kStatic>
-__device__ __forceinline__ void quantize_row(const void* __restrict__ x, long row, int L,
+__device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, long row, int L,
                                                   int lane, const float* __restrict__ static_a,
                                                   uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ sf,
