@@ -11,6 +11,7 @@ import synth
 from helpers import bf16_bits, dev, dev_bf16
 from oracle import moe as om
 from oracle import quant as oq
+from oracle import recipes as orc
 from oracle.formats import bf16_to_f32
 
 pytestmark = pytest.mark.gpu
@@ -132,29 +133,44 @@ def test_forward_route_quantize_boundary(pm, T):
     assert not bf16_bits(ref)[7].any()
 
 
+@pytest.mark.parametrize("recipe", ["per_token", "per_tensor"])
 @pytest.mark.parametrize("streams", [1, 2])
-def test_requant_bytes_in_the_path(pm, streams):
+def test_requant_bytes_in_the_path(pm, streams, recipe):
     """The intermediate's requantization inside the routed path, bit for bit:
-    hq, h_sf and h_scale that the path leaves in its workspace equal the
-    oracle's per-row quantization of the FP32 h it left beside them, for every
-    routed row. One stream runs one workgroup per row over all rows; two
-    streams run each expert half's rows one wave per row over a looping grid
-    (a ragged 132-block row: some lanes hold 3 blocks, others 2)."""
+    hq, h_sf (and h_scale, per-token) that the path leaves in its workspace
+    equal the oracle's quantization of the FP32 h it left beside them -- per
+    row, or with the static scale a2 -- for every routed row. One stream runs
+    one workgroup per row over all rows; two streams run each expert half's
+    rows one wave per row over a looping grid (a ragged 132-block row: some
+    lanes hold 3 blocks, others 2)."""
     import torch
     rng = np.random.default_rng(2112 + streams)
     T, K, E, H, I, act = 1024, 4, 16, 256, 2112, "relu2"
     ids = np.argsort(rng.standard_normal((T, E)), axis=1)[:, :K].astype(np.int32)
     ids[rng.random((T, K)) < 0.05] = -1
     w1, w2, x, wts, P = _moe_case(pm, rng, T, K, E, H, I, act, ids)
-    xq, xs, xg = pm.quantize_input_per_token(dev_bf16(x))
+    xd = dev_bf16(x)
     ws = torch.zeros(pm.moe_workspace_bytes(T, K, E, H, I, P.act), dtype=torch.uint8, device="cuda")
-    pm.routed_moe_ex(xq, xs, xg, dev(ids), dev(wts), P, workspace=ws, streams=streams)
+    if recipe == "per_token":
+        xq, xs, xg = pm.quantize_input_per_token(xd)
+        pm.routed_moe_ex(xq, xs, xg, dev(ids), dev(wts), P, workspace=ws, streams=streams)
+    else:
+        a1 = torch.tensor([float(2688.0 / np.abs(bf16_to_f32(x)).max())], device="cuda")
+        a2_host = np.float32(2688.0 / 0.75)
+        a2 = torch.tensor([float(a2_host)], dtype=torch.float32, device="cuda")
+        P = pm.prepare_weights(dev_bf16(w1), dev_bf16(w2), input_scales=(a1, a2))
+        xq, xs = pm.quantize_input_per_tensor(xd, a1)
+        pm.routed_moe_ex(xq, xs, None, dev(ids), dev(wts), P, recipe="per_tensor", a2=a2,
+                         workspace=ws, streams=streams)
     _sync()
     v = pm.workspace_views(ws, T, K, E, H, I, P.act)
     R = int(v["counters"][0].item())
     assert R == int((ids >= 0).sum())
     h = v["h"][:R].cpu().numpy()
-    q, s, g = oq.quantize_rows_f32(h)
+    if recipe == "per_token":
+        q, s, g = oq.quantize_rows_f32(h)
+        assert np.array_equal(v["h_scale"][:R].cpu().numpy().view(np.uint32), g.view(np.uint32))
+    else:
+        q, s = orc.quantize_rows_static(h, a2_host)
     assert np.array_equal(v["hq"][:R].cpu().numpy(), q)
     assert np.array_equal(v["h_sf"][:R].cpu().numpy(), s)
-    assert np.array_equal(v["h_scale"][:R].cpu().numpy().view(np.uint32), g.view(np.uint32))
