@@ -37,10 +37,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restric
     }
   }
   uint4 o;
-  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-  o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-  o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+  o.x = f32x2_to_bf16x2(acc[0], acc[1]);
+  o.y = f32x2_to_bf16x2(acc[2], acc[3]);
+  o.z = f32x2_to_bf16x2(acc[4], acc[5]);
+  o.w = f32x2_to_bf16x2(acc[6], acc[7]);
   *reinterpret_cast<uint4*>(out + (long)t * H + col) = o;
 }
 
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* __restri
   for (long i = blockIdx.x * 256L + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
     const float4 a = in[2 * i], b = in[2 * i + 1];
     uint4 o;
-    o.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
-    o.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
-    o.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
-    o.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+    o.x = f32x2_to_bf16x2(a.x, a.y);
+    o.y = f32x2_to_bf16x2(a.z, a.w);
+    o.z = f32x2_to_bf16x2(b.x, b.y);
+    o.w = f32x2_to_bf16x2(b.z, b.w);
     out[i] = o;
   }
 }
