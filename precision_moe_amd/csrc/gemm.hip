@@ -412,9 +412,17 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       for (int k = 0; k < kPassRows * kRowB / (64 * 16); ++k) {
         const int off = (k * 64 + lane) * 16;
         const int r = off / kRowB, cb = off % kRowB;
-        if (r < nrow && cb < row_bytes)
-          *reinterpret_cast<uint4*>(out + (long)r * P.out_stride * kS + cb) =
-              *reinterpret_cast<const uint4*>(wbuf + off);
+        if (r < nrow && cb < row_bytes) {
+          // FC1's h is written once and read once, by the next kernel:
+          // non-temporal stores keep it from displacing the weight slabs
+          // that the M-tiles of an expert share in L2
+          u32x4* dst = reinterpret_cast<u32x4*>(out + (long)r * P.out_stride * kS + cb);
+          const u32x4 val = *reinterpret_cast<const u32x4*>(wbuf + off);
+          if constexpr (MODE == kFc1Swiglu || MODE == kFc1Relu2)
+            __builtin_nontemporal_store(val, dst);
+          else
+            *dst = val;
+        }
       }
       if (r_lo + kPassRows < 16 * NRB) __syncthreads();  // the next pass overwrites the buffer
     }
