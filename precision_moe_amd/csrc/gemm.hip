@@ -61,6 +61,7 @@ constexpr int kStageK = 128;                       // reduction elements per LDS
 constexpr int kLdsRow = kStageK * 2;               // bytes per LDS A row (16 slots of 16 B)
 constexpr int kLdsStage = kTileM * kLdsRow;        // bytes per LDS stage buffer
 constexpr int kBufFlags = 0x00020000;              // raw buffer, 32-bit data format
+constexpr int kCpolNT = 2;                         // cache-policy operand: non-temporal
 constexpr int kGroup = 2;                          // stages per loop iteration
 constexpr int kStages = 2;                         // LDS A stage buffers (double buffer)
 // B register ring (chunks per wave, RING - 1 of them in flight) and resident
@@ -113,11 +114,12 @@ struct BFrag {
 };
 
 // Main loop + epilogue for one tile. NRB: the tile's rows rounded up to 16-row
-// blocks (1..4); blocks past it are neither staged nor multiplied. Every global
+// blocks (1..4); blocks past it are neither staged nor multiplied. kNT = 1:
+// the weight loads carry the non-temporal hint (slabs read by this tile only). Every global
 // load inside the loop is unconditional (addresses past the end are out of the
 // buffer range and return zeros, and that data is never used), which keeps the
 // in-order load counters exact so the B ring really stays in flight.
-template <int MODE, int NRB, int AK, int kRing>
+template <int MODE, int NRB, int AK, int kRing, int kNT>
 __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
                                         int mrows, int nt) {
@@ -207,11 +209,13 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   const int sdw = (lane & 15) + 16 * (lane >> 5);  // this lane's scale dword of a position
   const int bs_voff0 = pos0 * 128 + sdw * 4, bs_voff1 = bs_voff0 + 128;
   auto load_q = [&](int voff, int c) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bq, voff, c * (kColTileBlocks * 1024), 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bq, voff, c * (kColTileBlocks * 1024),
+                                                          kNT ? kCpolNT : 0);
     return make_uint4(v.x, v.y, v.z, v.w);
   };
   auto load_s = [&](int voff, int c) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bs, voff, c * (kColTileBlocks * 128), 0);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bs, voff, c * (kColTileBlocks * 128),
+                                                          kNT ? kCpolNT : 0);
   };
 
   // acc[rb][cb]: 16-row block rb, 16-column block cb of the wave's 64 columns
@@ -429,6 +433,16 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   }
 }
 
+template <int MODE, int NRB, int AK, int kRing>
+__device__ __forceinline__ void tile_nt(bool single, const FcParams& P, uint8_t (*a_lds)[kLdsStage],
+                                        const int* a_row, const float* s_row, int e, int row0,
+                                        int mrows, int nt) {
+  if (single)
+    fc_tile<MODE, NRB, AK, kRing, 1>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
+  else
+    fc_tile<MODE, NRB, AK, kRing, 0>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
+}
+
 template <int MODE, int AK, int kRing>
 __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                          int* a_row, float* s_row) {
@@ -466,10 +480,13 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
   }
   __syncthreads();
   switch ((mrows + 15) >> 4) {  // 16-row blocks that hold rows of this tile
-    case 1: fc_tile<MODE, 1, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    case 2: fc_tile<MODE, 2, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    case 3: fc_tile<MODE, 3, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
-    default: fc_tile<MODE, 4, AK, kRing>(P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    // An expert with one M-tile reads its weight slabs once: its B loads are
+    // non-temporal (kNT), so they do not displace the slabs that the M-tiles
+    // of a multi-tile expert share in L2.
+    case 1: tile_nt<MODE, 1, AK, kRing>(count == 1, P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 2: tile_nt<MODE, 2, AK, kRing>(count == 1, P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    case 3: tile_nt<MODE, 3, AK, kRing>(count == 1, P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
+    default: tile_nt<MODE, 4, AK, kRing>(count == 1, P, a_lds, a_row, s_row, e, row0, mrows, nt); break;
   }
 }
 
