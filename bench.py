@@ -1,23 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the per-token NVFP4 routed-MoE hot path on one MI355X.
 
-One step = pmoe_moe_forward on BF16 activations (per-token quantization
-overlapped with the routing, FC1 + activation, requantization, FC2,
-fixed-order finalize) over one batch of
-synthetic tokens already resident in HBM, with weights prepared beforehand
-(preparation is timed separately and reported as `prepare`).
+One step = pmoe_moe_forward on BF16 activations (per-token quantization in
+the same launch as the routing, FC1 + activation, requantization, FC2,
+fixed-order finalize) over one batch of synthetic tokens already resident in
+HBM, with weights prepared beforehand (preparation is timed separately and
+reported as `prepare`).
 
 Default workload: the one-GPU share of an EP4 MoE layer -- E=96 local experts,
 H=7168, I=3072, SwiGLU, top-6, T=1024 tokens, two hot experts (router logits
 +2 on experts 0 and 48); inputs from the seeded generator in synth/.
 
-Prints one JSON line. `roofline` is the dominant kernel (FC1 grouped GEMM):
-algorithmic bytes per launch over its average duration, measured here with
-HIP events around that step on the stream it runs on. `cpu_baseline` times
-the CPU oracle on a bounded sample (all routes of the first --cpu-experts
-experts). `device` reports this device's own ceilings: the bandwidth of a plain
-1 GiB device-to-device copy, and the graphics clock and socket power sampled
-while the step runs back to back.
+Prints one JSON line. `value` is tokens/s over the K bracketed steps; `step_us`
+gives the median and p10/p90 of K more steps timed one by one. `roofline` is
+the dominant kernel, the FC1 grouped GEMM as the step runs it: two launches
+(one per part of the experts) on two streams; its algorithmic bytes over the
+span from the first launch's start to the last launch's end, measured with
+HIP events recorded on the stream each launch runs on (the library records
+them around its own launches). `other_workloads` gives the same figures for
+further workloads, `cpu_baseline` the CPU oracle on a bounded sample (all routes
+of the first --cpu-experts experts), and `device` this device's own ceilings:
+the bandwidth of a plain 1 GiB device-to-device copy, and the graphics clock
+and socket power sampled while the step runs back to back.
 """
 import argparse
 import json
@@ -51,6 +55,8 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-experts", type=int, default=20,
                     help="the CPU oracle baseline runs all routes of this many experts")
+    ap.add_argument("--other-workloads", default="ep4_t512,large",
+                    help="comma-separated further workloads timed in the same run ('' for none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(calibrates the HBM byte counters) and exit")
@@ -177,6 +183,111 @@ def clock_under_load(torch, fn, seconds=1.0):
             "note": "amdsmi GPU metrics, median over the samples taken while the step ran"}
 
 
+def percentiles_us(ms_list):
+    a = np.asarray(ms_list, np.float64) * 1e3
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def source_id():
+    """The git commit when run from a checkout, and a hash of the library and bench sources
+    (the GPU host gets a copy of the tree without its history)."""
+    import hashlib
+    import subprocess
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "precision_moe_amd", "csrc")
+    for p in sorted(os.listdir(csrc)) + ["../../include/pmoe.h", "../../bench.py"]:
+        with open(os.path.join(csrc, p), "rb") as f:
+            h.update(f.read())
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        sha = None
+    return {"git_sha": sha, "source_sha256": h.hexdigest()[:16]}
+
+
+def timed_steps(torch, fn, steps):
+    """K calls of fn, each between two events on torch's current stream: per-step ms."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def gemm_spans(torch, pm, fn, steps):
+    """K steps with the library's step events: per step, the FC1 span (first FC1 launch's
+    start to the last one's end, over both streams), the FC2 span, and each part's own FC1
+    and FC2 launch times (ms)."""
+    per = [[torch.cuda.Event(enable_timing=True) for _ in range(pm.STEP_EVENTS)] for _ in range(steps)]
+    for evs in per:
+        for e in evs:
+            e.record()                      # creates the events; the library records them again
+    torch.cuda.synchronize()
+    for evs in per:
+        fn(evs)
+    torch.cuda.synchronize()
+    out = {"fc1_span": [], "fc2_span": [], "fc1_part1": [], "fc1_part2": [], "fc2_part1": [],
+           "fc2_part2": []}
+    for e in per:
+        t = lambda i, j: e[i].elapsed_time(e[j])           # ms from event i to event j
+        out["fc1_span"].append(max(t(0, 1), t(0, 3)) - min(0.0, t(0, 2)))
+        out["fc2_span"].append(max(t(4, 5), t(4, 7)) - min(0.0, t(4, 6)))
+        out["fc1_part1"].append(t(0, 1))
+        out["fc1_part2"].append(t(2, 3))
+        out["fc2_part1"].append(t(4, 5))
+        out["fc2_part2"].append(t(6, 7))
+    return out
+
+
+def run_workload(torch, pm, synth, w, P, dev, steps, warmup):
+    """Step time distribution, throughput and in-step GEMM figures of one workload."""
+    x = synth.activations(w, device=dev).view(torch.bfloat16)
+    ids_np, wts_np = synth.router(w)
+    ids = torch.from_numpy(ids_np).to(dev)
+    wts = torch.from_numpy(wts_np).to(dev)
+    ws = torch.empty(pm.moe_workspace_bytes(w.T, w.K, w.E, w.H, w.I, P.act), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+
+    def step(step_events=None):
+        pm.moe_forward(x, ids, wts, P, workspace=ws, out=out, step_events=step_events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    dist = timed_steps(torch, step, steps)
+    spans = gemm_spans(torch, pm, step, steps)
+    views = pm.workspace_views(ws, w.T, w.K, w.E, w.H, w.I, P.act)
+    counts = np.diff(views["expert_offsets"].cpu().numpy())
+    R = int(counts.sum())
+    ab = algorithmic_bytes(w, counts, w.T, R)
+    ms = float(np.mean(dist))
+    flops = 2.0 * R * (w.N1 * w.H + w.H * w.I)
+    fc1 = float(np.mean(spans["fc1_span"]))
+    fc2 = float(np.mean(spans["fc2_span"]))
+    res = {
+        "workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.K, "act": w.act,
+        "routed_rows": R, "step_us": percentiles_us(dist), "tokens/s": w.T / (ms * 1e-3),
+        "TFLOP/s": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "fc1_in_step": {"span_us": fc1 * 1e3, "GB/s": ab["fc1"] / (fc1 * 1e-3) / 1e9,
+                        "hbm_frac": ab["fc1"] / (fc1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "TFLOP/s": 2.0 * R * w.N1 * w.H / (fc1 * 1e-3) / 1e12,
+                        "mfma_frac": 2.0 * R * w.N1 * w.H / (fc1 * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                        "algorithmic_bytes": ab["fc1"]},
+        "fc2_in_step": {"span_us": fc2 * 1e3, "GB/s": ab["fc2"] / (fc2 * 1e-3) / 1e9,
+                        "hbm_frac": ab["fc2"] / (fc2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "TFLOP/s": 2.0 * R * w.H * w.I / (fc2 * 1e-3) / 1e12,
+                        "mfma_frac": 2.0 * R * w.H * w.I / (fc2 * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                        "algorithmic_bytes": ab["fc2"]},
+        "launch_us": {k: float(np.mean(v)) * 1e3 for k, v in spans.items() if "part" in k},
+    }
+    return res, dict(x=x, ids=ids, wts=wts, ids_np=ids_np, wts_np=wts_np, ws=ws, out=out, step=step,
+                     views=views, counts=counts, R=R, ab=ab, spans=spans)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -210,18 +321,12 @@ def main():
     w2 = w2.view(torch.bfloat16)
     P = pm.prepare_weights(w1, w2)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    e0.record()
-    for _ in range(reps):
-        pm.prepare_weights(w1, w2, out=P)
-    e1.record()
-    torch.cuda.synchronize()
-    prep_ms = e0.elapsed_time(e1) / reps
+    prep_ms = timed_steps(torch, lambda: pm.prepare_weights(w1, w2, out=P), 3)
+    prep = float(np.mean(prep_ms))
     elems = w.E * (w.N1 * w.H + w.H * w.I)
-    prepare = {"ms": prep_ms, "GB/s": elems * (2 + NVFP4_BYTES) / (prep_ms * 1e-3) / 1e9,
+    prepare = {"ms": prep, "GB/s": elems * (2 + NVFP4_BYTES) / (prep * 1e-3) / 1e9,
                "note": "reads BF16 once (algorithmic; the kernel reads it twice) and writes NVFP4"}
-    log(f"[bench] prepare_weights {prep_ms:.2f} ms")
+    log(f"[bench] prepare_weights {prep:.2f} ms")
 
     # ---------------------------------------------------------------- inputs
     x = synth.activations(w, device=dev).view(torch.bfloat16)
@@ -235,8 +340,8 @@ def main():
     ws = torch.empty(pm.moe_workspace_bytes(T, w.K, w.E, w.H, w.I, P.act), dtype=torch.uint8, device=dev)
     out = torch.empty((T, w.H), dtype=torch.bfloat16, device=dev)
 
-    def step():
-        pm.moe_forward(x, ids, wts, P, workspace=ws, out=out)
+    def step(step_events=None):
+        pm.moe_forward(x, ids, wts, P, workspace=ws, out=out, step_events=step_events)
 
     def step_separate_quantize():
         pm.quantize_input_per_token(x, out=(xq, xs, xg))
@@ -257,19 +362,21 @@ def main():
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
 
-    # ---------------------------------------------------------------- FC1 alone
-    # Inside a step the two expert halves run FC1 on two streams, overlapped
-    # with the other half's work; the roofline figure times the whole FC1
-    # kernel (one launch over all experts, the same code) with HIP events on
-    # the stream it runs on, over as many launches as the timed region had.
-    fc1_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    for a, b in fc1_evs:
-        a.record()
-        pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_FC1, pm.STEP_FC1))
-        b.record()
-    torch.cuda.synchronize()
-    fc1_ms_timed = float(np.mean([a.elapsed_time(b) for a, b in fc1_evs]))
+    # ---------------------------------------------------------------- step distribution
+    # K more steps, each between two events: median and p10/p90 of the step time
+    dist = timed_steps(torch, step, args.steps)
+    # K more steps with the library's step events: the grouped GEMMs as the step runs them
+    spans = gemm_spans(torch, pm, step, args.steps)
+    log(f"[bench] step median {np.median(dist) * 1e3:.1f} us; in-step FC1 span "
+        f"{np.mean(spans['fc1_span']) * 1e3:.1f} us, FC2 span {np.mean(spans['fc2_span']) * 1e3:.1f} us")
+
+    # ---------------------------------------------------------------- whole FC1 launch
+    # Secondary figure: FC1 over all experts as one launch (fc_kernel, the one-stream
+    # path's kernel) on the quantized activations of this workload, timed alone.
+    pm.quantize_input_per_token(x, out=(xq, xs, xg))
+    pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(pm.STEP_ROUTE, pm.STEP_ROUTE))
+    fc1_whole = timed_steps(torch, lambda: pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out,
+                                                         steps=(pm.STEP_FC1, pm.STEP_FC1)), args.steps)
 
     # ---------------------------------------------------------------- per-step events
     names = ["quantize", "route", "fc1", "requant", "fc2", "finalize"]
@@ -279,9 +386,9 @@ def main():
         evs[0].record()
         pm.quantize_input_per_token(x, out=(xq, xs, xg))
         evs[1].record()
-        for s in range(5):
-            pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(s, s))
-            evs[s + 2].record()
+        for st in range(5):
+            pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out, steps=(st, st))
+            evs[st + 2].record()
         torch.cuda.synchronize()
         acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
     stage_ms = acc / args.stage_reps
@@ -292,6 +399,7 @@ def main():
     # The per-tensor NVFP4 and W4A16 variants of the same layer, on the same
     # inputs: static scales calibrated as 2688 / amax of the FC1 input and of
     # the per-token run's intermediate (setup, outside the timed region).
+    pm.routed_moe(xq, xs, xg, ids, wts, P, workspace=ws, out=out)
     R_rows = int(views["counters"][0].item())
     a1 = (2688.0 / x.float().abs().max()).reshape(1).float()
     a2 = (2688.0 / views["h"][:R_rows].abs().max()).reshape(1).float()
@@ -332,13 +440,7 @@ def main():
         for _ in range(max(args.warmup // 2, 2)):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        ms = float(np.mean(timed_steps(torch, fn, args.steps)))
         recipes[name] = {"ms_per_step": ms, "tokens/s": T / (ms * 1e-3)}
         if name != "router_topk":
             recipes[name]["TFLOP/s"] = flops_step / (ms * 1e-3) / 1e12
@@ -363,13 +465,16 @@ def main():
         k["hbm_frac"] = k["GB/s"] / PEAK_HBM_GBS
     flops = 2.0 * R * (w.N1 * w.H + w.H * w.I)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    fc1_flops = 2.0 * R * w.N1 * w.H
-    kernels["fc1"]["TFLOP/s"] = float(fc1_flops / (stage_ms[2] * 1e-3) / 1e12)
+    kernels["fc1"]["TFLOP/s"] = float(2.0 * R * w.N1 * w.H / (stage_ms[2] * 1e-3) / 1e12)
     kernels["fc2"]["TFLOP/s"] = float(2.0 * R * w.H * w.I / (stage_ms[4] * 1e-3) / 1e12)
     for n in ("fc1", "fc2"):
         kernels[n]["mfma_frac"] = kernels[n]["TFLOP/s"] / PEAK_F16_TFLOPS
-    fc1_gbs = ab["fc1"] / (fc1_ms_timed * 1e-3) / 1e9
+    fc1_span = float(np.mean(spans["fc1_span"]))
+    fc2_span = float(np.mean(spans["fc2_span"]))
+    fc1_gbs = ab["fc1"] / (fc1_span * 1e-3) / 1e9
+    fc1_whole_ms = float(np.mean(fc1_whole))
     traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", f"fc1_{w.name}_hbm_traffic.txt"), w.name)
+    kern = ("pmoe::fc_half_kernel<1, 0>" if w.gated else "pmoe::fc_half_kernel<0, 0>")
 
     result = {
         "metric": METRIC,
@@ -382,19 +487,40 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "nvfp4",
+        "compute": "NVFP4 W4A4 (E2M1 codes, E4M3 block scales per 16, FP32 per-token / per-expert "
+                   "scales) decoded exactly to FP16 operands of v_mfma_f32_16x16x32_f16, FP32 "
+                   "accumulation; BF16 output",
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.K,
                    "act": w.act, "routed_rows": R, "parallelism": "none (1 GPU)"},
+        "source": source_id(),
+        "step_us": percentiles_us(dist),
         "tflops": tflops,
         "mfma_frac": tflops / PEAK_F16_TFLOPS,
         "hbm_frac_step": ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "roofline": {"bound": "hbm", "kernel": "fc1 grouped GEMM (SwiGLU epilogue)" if w.gated else
-                     "fc1 grouped GEMM (squared-ReLU epilogue)",
+        "roofline": {"bound": "hbm", "kernel": kern,
+                     "what": "FC1 grouped GEMM as the step runs it: one launch per part of the "
+                             "experts, on two streams; achieved = algorithmic bytes of the whole FC1 "
+                             "over the span from the first launch's start to the last one's end "
+                             "(HIP events recorded by the library on each launch's stream), mean over "
+                             "the steps",
                      "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes": ab["fc1"], "avg_launch_us": fc1_ms_timed * 1e3,
+                     "algorithmic_bytes": ab["fc1"], "span_us": fc1_span * 1e3,
+                     "span_us_median": float(np.median(spans["fc1_span"])) * 1e3,
+                     "launch_us": {"part1": float(np.mean(spans["fc1_part1"])) * 1e3,
+                                   "part2": float(np.mean(spans["fc1_part2"])) * 1e3},
+                     "whole_launch": {"kernel": "pmoe::fc_kernel (all experts, one launch, alone)",
+                                      "avg_launch_us": fc1_whole_ms * 1e3,
+                                      "GB/s": ab["fc1"] / (fc1_whole_ms * 1e-3) / 1e9,
+                                      "frac": ab["fc1"] / (fc1_whole_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
                      "device_copy_GBps": copy_gbs, "frac_of_device_copy": fc1_gbs / copy_gbs},
+        "fc2_in_step": {"span_us": fc2_span * 1e3, "GB/s": ab["fc2"] / (fc2_span * 1e-3) / 1e9,
+                        "hbm_frac": ab["fc2"] / (fc2_span * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "algorithmic_bytes": ab["fc2"],
+                        "launch_us": {"part1": float(np.mean(spans["fc2_part1"])) * 1e3,
+                                      "part2": float(np.mean(spans["fc2_part2"])) * 1e3}},
         "device": {"copy_GBps": copy_gbs, "gfx_mhz_under_load": clock["gfx_mhz"],
                    "socket_w_under_load": clock["socket_w"], "clock_samples": clock["samples"],
                    "clock_note": clock["note"], "nominal_mhz": NOMINAL_MHZ,
@@ -404,6 +530,32 @@ def main():
         "prepare": prepare,
         "recipes": recipes,
     }
+
+    # ---------------------------------------------------------------- other workloads
+    others = {}
+    del ws, out, views
+    torch.cuda.empty_cache()
+    for name in [n for n in args.other_workloads.split(",") if n]:
+        ow = synth.WORKLOADS[name]
+        same = (ow.index, ow.weight_epoch, ow.E, ow.N1, ow.H, ow.I) == (w.index, w.weight_epoch, w.E,
+                                                                        w.N1, w.H, w.I)
+        if same:
+            OP = P
+        else:
+            P = None
+            torch.cuda.empty_cache()
+            a, b = synth.all_weights(ow, device=dev)
+            OP = pm.prepare_weights(a.view(torch.bfloat16), b.view(torch.bfloat16))
+            del a, b
+            torch.cuda.empty_cache()
+        res, _ = run_workload(torch, pm, synth, ow, OP, dev, args.steps, max(args.warmup, 5))
+        others[name] = res
+        log(f"[bench] {name}: median {res['step_us']['median']:.1f} us/step, "
+            f"{res['tokens/s'] / 1e6:.3f} M tokens/s, FC1 span {res['fc1_in_step']['span_us']:.1f} us")
+        del OP
+        torch.cuda.empty_cache()
+    result["other_workloads"] = others
+
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(w, ids_np, wts_np, args.cpu_experts)

@@ -32,9 +32,14 @@
  * (weights, "alpha") [Megatron-LM #8262 . Background; FlashInfer #5019 . Tensor
  * and numerical contract]. BF16 tensors are passed as raw 16-bit storage.
  *
- * Shape limits of this build: H and I multiples of 64 in [64, 16384];
- * 1 <= K <= min(32, E); 1 <= E <= 1024; T >= 0 (T == 0 is a successful no-op);
- * T*H and T*K*I below 2^31.
+ * Shape limits of this build: H and I multiples of 16 (one block) in
+ * [16, 16384]; 1 <= K <= min(32, E); 1 <= E <= 1024; T >= 0 (T == 0 is a
+ * successful no-op); T*Hp and T*K*Ip below 2^31, where Hp and Ip are H and I
+ * rounded up to a multiple of 64 (the W4A16 recipe: 2*T*Hp and 2*T*K*Ip). The
+ * grouped GEMMs reduce over whole chunks of 64 elements: a reduction length
+ * that is not a multiple of 64 is padded inside the library with zero codes
+ * and zero block scales, which add exactly zero to every sum; the canonical
+ * arrays at this interface are never padded.
  */
 #ifndef PMOE_H_
 #define PMOE_H_
@@ -79,9 +84,11 @@ const char* pmoe_last_error(void);
  * Prepared (kernel-native) layout of one FC matrix with logical shape
  * [E, N, Kd] (N output rows, Kd the reduction length; FC1: N = N1, Kd = H;
  * FC2: N = H, Kd = I). Rows are grouped in blocks of 32 ("col blocks" p,
- * NB = N/32, padded with all-zero blocks to NBp = NB rounded up to a multiple
- * of 8), blocks in column tiles of 8 (ct = p/8, pos = p%8, NT = NBp/8), and
- * the reduction in chunks of 64 (c, KC = Kd/64). Chunk c of a column tile --
+ * NB = ceil(N/32), or 2*ceil(I/32) for a gated FC1; padded with all-zero
+ * blocks to NBp = NB rounded up to a multiple of 8), blocks in column tiles
+ * of 8 (ct = p/8, pos = p%8, NT = NBp/8), and the reduction in chunks of 64
+ * (c, KC = ceil(Kd/64); the elements in [Kd, 64*KC) are zero). Rows of a block
+ * past the matrix (past I in each half of a gated FC1) are zero. Chunk c of a column tile --
  * all 8 of its blocks -- is one contiguous slab, so a GEMM workgroup owning
  * the tile streams a single sequential region:
  *
@@ -99,13 +106,14 @@ const char* pmoe_last_error(void);
  * Row map n(p, col): non-gated FC1 and FC2: n = 32*p + col. Gated FC1 (N1 = 2I)
  * interleaves gate and up blocks so one workgroup holds both halves of a SwiGLU
  * output: p even -> gate row 32*(p/2) + col; p odd -> up row I + 32*(p/2) + col
+ * (for 32*(p/2) + col < I)
  * (gate rows are [0, I), up rows [I, 2I) of the canonical FC1 [FlashInfer #5019 .
  * Tensor and numerical contract, 'gate-then-up']).
  *
  * The bytes are the canonical codes/scales of the per-expert NVFP4 recipe
  * (packed [E, N, Kd/2], linear scales [E, N, Kd/16]) permuted by this map
- * (padding blocks are zero); no value is changed and alpha is never folded
- * into the block scales.
+ * (padding is zero); no value is changed and alpha is never folded into the
+ * block scales.
  */
 
 /* Sizes in bytes of the four prepared arrays: sizes[0] FC1 codes, sizes[1] FC1
@@ -193,7 +201,7 @@ int pmoe_quantize_input_per_tensor(const void* x, int T, int H, const float* a1_
  * the FP32 expert intermediate before FC2 [Megatron-LM #8262 . How to extend,
  * 'fc2_input_scale'; What is tested, 4. Train-gen parity]. routed_moe runs this
  * quantizer on its intermediate; it is exported so it can be checked alone.
- *   h : float32 [R, L], L a multiple of 64 up to 16384;  hq : uint8 [R, L/2];
+ *   h : float32 [R, L], L a multiple of 16 up to 16384;  hq : uint8 [R, L/2];
  *   h_sf : uint8 [R, L/16];  h_scale : float32 [R].
  */
 int pmoe_quantize_rows_f32(const float* h, int R, int L,
@@ -211,9 +219,10 @@ size_t pmoe_moe_workspace_bytes(int T, int K, int E, int H, int I, int act);
 #define PMOE_WS_COUNTERS 3       /* int32 [4]     {R, number of M-tiles, first M-tile and first row
                                     of the experts run on the second stream}                    */
 #define PMOE_WS_H 4              /* float32 [T*K, I]   activation output (rows < R valid);
-                                    BF16 [T*K, I] under pmoe_routed_moe_w4a16                   */
-#define PMOE_WS_HQ 5             /* uint8 [T*K, I/2]   requantized intermediate codes              */
-#define PMOE_WS_H_SF 6           /* uint8 [T*K, I/16]  its E4M3 block scales                        */
+                                    BF16 [T*K, Ip] under pmoe_routed_moe_w4a16 (Ip = I rounded
+                                    up to 64; columns past I are 0)                             */
+#define PMOE_WS_HQ 5             /* uint8 [T*K, Ip/2]  requantized intermediate codes (past I/2: 0) */
+#define PMOE_WS_H_SF 6           /* uint8 [T*K, Ip/16] its E4M3 block scales (past I/16: 0)         */
 #define PMOE_WS_H_SCALE 7        /* float32 [T*K]      its per-row scales (per-token recipe only)   */
 #define PMOE_WS_Z 8              /* BF16 [T*K, H]      per-route FC2 outputs                         */
 #define PMOE_WS_NUM_FIELDS 9
@@ -249,7 +258,10 @@ int pmoe_moe_workspace_layout(int T, int K, int E, int H, int I, int act,
  * accumulated in FP32 from +0 without fused multiply-add. A token with no
  * valid route gets +0. The result of a token depends only on its own inputs
  * (batch invariant): the tiling never depends on T and no split-K is used.
- * Alignment: every pointer 16 bytes, except x_scale/topk_w/topk_ids 4 bytes.
+ * Alignment: ws 256 bytes (its fields start on 256-byte boundaries); int64
+ * topk_ids 8 bytes, int32 topk_ids, x_scale and topk_w 4 bytes; every other
+ * pointer 16 bytes. A misaligned pointer is PMOE_ERR_POINTER. The same rules hold
+ * for every entry point below that takes these arguments.
  */
 int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
                     const void* topk_ids, int ids_type, const float* topk_w,
@@ -337,7 +349,17 @@ typedef struct pmoe_moe_options {
                              finalize (same bits either way; needs E >= 2)              */
   const float* a1_scale;  /* pmoe_moe_forward, per-tensor recipe: device float32 scalar
                              (the static FC1 input scale); otherwise NULL               */
+  void* const* step_events; /* NULL, or PMOE_STEP_EVENTS caller-created hipEvent_t handles
+                             (created with timing enabled, for timing only: not under
+                             graph capture), recorded on the stream that runs each
+                             grouped GEMM: [0]/[1] before/after FC1 of the first part
+                             of the experts, [2]/[3] FC1 of the second part, [4]/[5] FC2
+                             of the first part, [6]/[7] FC2 of the second part. With
+                             one stream both pairs of a GEMM are recorded around its
+                             one launch. A NULL entry is skipped.                     */
 } pmoe_moe_options;
+
+#define PMOE_STEP_EVENTS 8
 
 /*
  * The routed path with options; options == NULL means per-token, ordered, no

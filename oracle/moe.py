@@ -171,10 +171,12 @@ class LazyWeights:
     """Weights quantized per expert on first use, for stacks too large to hold.
 
     `source(e)` returns (w1_bf16 [N1, H], w2_bf16 [H, I]) of expert e.
+    `cache` (optional) is the dict that keeps the quantized experts, so several
+    instances over the same source can share one.
     """
 
-    def __init__(self, source, E, N1, H, I):
-        self._source, self._cache = source, {}
+    def __init__(self, source, E, N1, H, I, cache=None):
+        self._source, self._cache = source, ({} if cache is None else cache)
         self._shape = (E, N1, H, I)
         detect_gating(N1, I)
 

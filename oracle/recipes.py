@@ -90,11 +90,13 @@ class LazyWeightsPerTensor:
     """Per-tensor weights quantized per expert on first use (stacks too large to hold).
 
     `source(e)` returns (w1_bf16 [N1, H], w2_bf16 [H, I]) of expert e; a1, a2 are
-    folded into that expert's alphas (reading R21).
+    folded into that expert's alphas (reading R21). `cache` (optional) is the
+    dict that keeps the quantized experts, shared by instances with the same
+    source and scales.
     """
 
-    def __init__(self, source, E, N1, H, I, a1, a2):
-        self._source, self._cache = source, {}
+    def __init__(self, source, E, N1, H, I, a1, a2, cache=None):
+        self._source, self._cache = source, ({} if cache is None else cache)
         self._shape = (E, N1, H, I)
         self._a1, self._a2 = F32(a1), F32(a2)
         detect_gating(N1, I)

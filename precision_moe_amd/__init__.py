@@ -32,7 +32,9 @@ class MoeOptions(ctypes.Structure):
     """pmoe_moe_options (include/pmoe.h)."""
     _fields_ = [("recipe", ctypes.c_int), ("finalize", ctypes.c_int),
                 ("swiglu_limit", ctypes.c_float), ("a2_scale", ctypes.c_void_p),
-                ("streams", ctypes.c_int), ("a1_scale", ctypes.c_void_p)]
+                ("streams", ctypes.c_int), ("a1_scale", ctypes.c_void_p),
+                ("step_events", ctypes.c_void_p)]
+STEP_EVENTS = 8
 _SIGNATURES = {
     "pmoe_version": (_i, []),
     "pmoe_last_error": (ctypes.c_char_p, []),
@@ -98,10 +100,38 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _stream(stream=None):
+def _stream(stream=None, *tensors):
+    """The hipStream_t to enqueue on. A `stream` other than torch's current one first
+    waits for the current stream (the inputs and the temporaries made here were produced
+    there), and every tensor the call touches is recorded as used on `stream`, so the
+    caching allocator does not hand its memory out again before that work is done."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        return ctypes.c_void_p(cur.cuda_stream)
+    stream.wait_stream(cur)
+    for t in tensors:
+        if t is not None and torch.is_tensor(t) and t.is_cuda:
+            t.record_stream(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _event_array(events):
+    """ctypes array of the raw hipEvent_t handles of STEP_EVENTS torch.cuda.Events (or None)."""
+    import torch
+    if events is None:
+        return None
+    if len(events) != STEP_EVENTS:
+        raise ValueError(f"step_events needs {STEP_EVENTS} events")
+    handles = []
+    for ev in events:
+        if ev is None:
+            handles.append(None)
+            continue
+        if ev.cuda_event == 0:          # torch creates the event on its first record
+            ev.record(torch.cuda.current_stream())
+        handles.append(ev.cuda_event)
+    return (ctypes.c_void_p * STEP_EVENTS)(*handles)
 
 
 def _bf16_storage(t):
@@ -170,13 +200,17 @@ def prepare_weights(w1, w2, out=None, workspace=None, stream=None, input_scales=
         _check(lib().pmoe_prepare_weights(
             _ptr(w1), _ptr(w2), E, N1, H, I, _ptr(out.w1_codes), _ptr(out.w1_scales),
             _ptr(out.w1_alpha), _ptr(out.w2_codes), _ptr(out.w2_scales), _ptr(out.w2_alpha),
-            _ptr(workspace), workspace.numel(), _stream(stream)))
+            _ptr(workspace), workspace.numel(), _stream(stream, w1, w2, workspace, out.w1_codes, out.w1_scales,
+                                                          out.w1_alpha, out.w2_codes, out.w2_scales,
+                                                          out.w2_alpha)))
     else:
         a1, a2 = (_f32_scalar(a) for a in input_scales)
         _check(lib().pmoe_prepare_weights_per_tensor(
             _ptr(w1), _ptr(w2), E, N1, H, I, _ptr(a1), _ptr(a2), _ptr(out.w1_codes),
             _ptr(out.w1_scales), _ptr(out.w1_alpha), _ptr(out.w2_codes), _ptr(out.w2_scales),
-            _ptr(out.w2_alpha), _ptr(workspace), workspace.numel(), _stream(stream)))
+            _ptr(out.w2_alpha), _ptr(workspace), workspace.numel(),
+            _stream(stream, w1, w2, a1, a2, workspace, out.w1_codes, out.w1_scales, out.w1_alpha,
+                    out.w2_codes, out.w2_scales, out.w2_alpha)))
     return out
 
 
@@ -199,7 +233,7 @@ def quantize_input_per_token(x, out=None, stream=None):
                torch.empty((T,), dtype=torch.float32, device=x.device))
     xq, xsf, xs = out
     _check(lib().pmoe_quantize_input_per_token(_ptr(x), T, H, _ptr(xq), _ptr(xsf), _ptr(xs),
-                                               _stream(stream)))
+                                               _stream(stream, x, xq, xsf, xs)))
     return xq, xsf, xs
 
 
@@ -213,7 +247,7 @@ def quantize_input_per_tensor(x, a1, out=None, stream=None):
                torch.empty((T, H // 16), dtype=torch.uint8, device=x.device))
     xq, xsf = out
     _check(lib().pmoe_quantize_input_per_tensor(_ptr(x), T, H, _ptr(_f32_scalar(a1)), _ptr(xq),
-                                                _ptr(xsf), _stream(stream)))
+                                                _ptr(xsf), _stream(stream, x, a1, xq, xsf)))
     return xq, xsf
 
 
@@ -229,7 +263,8 @@ def quantize_rows_f32(h, out=None, stream=None):
                torch.empty((R, L // 16), dtype=torch.uint8, device=h.device),
                torch.empty((R,), dtype=torch.float32, device=h.device))
     hq, hsf, hs = out
-    _check(lib().pmoe_quantize_rows_f32(_ptr(h), R, L, _ptr(hq), _ptr(hsf), _ptr(hs), _stream(stream)))
+    _check(lib().pmoe_quantize_rows_f32(_ptr(h), R, L, _ptr(hq), _ptr(hsf), _ptr(hs),
+                                        _stream(stream, h, hq, hsf, hs)))
     return hq, hsf, hs
 
 
@@ -252,6 +287,7 @@ def workspace_views(ws, T, K, E, H, I, act):
     import torch
     off = moe_workspace_layout(T, K, E, H, I, act)
     TK = T * K
+    Ip = -(-I // 64) * 64          # the intermediate's rows are padded to whole 64-element chunks
 
     def view(name, count, dtype):
         nbytes = count * torch.empty((), dtype=dtype).element_size()
@@ -263,9 +299,12 @@ def workspace_views(ws, T, K, E, H, I, act):
         "expert_offsets": view("expert_offsets", E + 1, torch.int32),
         "counters": view("counters", 4, torch.int32),
         "h": view("h", TK * I, torch.float32).view(TK, I),
-        "h_bf16": view("h", TK * I, torch.int16).view(TK, I),    # W4A16: BF16 h in the same field
-        "hq": view("hq", TK * I // 2, torch.uint8).view(TK, I // 2),
-        "h_sf": view("h_sf", TK * I // 16, torch.uint8).view(TK, I // 16),
+        # W4A16: BF16 h in the same field, rows of Ip (zeros past I)
+        "h_bf16": view("h", TK * Ip, torch.int16).view(TK, Ip)[:, :I],
+        "hq": view("hq", TK * Ip // 2, torch.uint8).view(TK, Ip // 2)[:, :I // 2],
+        "h_sf": view("h_sf", TK * Ip // 16, torch.uint8).view(TK, Ip // 16)[:, :I // 16],
+        "hq_padded": view("hq", TK * Ip // 2, torch.uint8).view(TK, Ip // 2),
+        "h_sf_padded": view("h_sf", TK * Ip // 16, torch.uint8).view(TK, Ip // 16),
         "h_scale": view("h_scale", TK, torch.float32),
         "z": view("z", TK * H, torch.int16).view(TK, H),
     }
@@ -303,7 +342,8 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, ac
         first, last, _ptr(xq), _ptr(x_sf), _ptr(x_scale), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K,
         W.E, W.H, W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
         _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, _ptr(workspace),
-        workspace.numel(), _ptr(out), _stream(stream)))
+        workspace.numel(), _ptr(out),
+        _stream(stream, xq, x_sf, x_scale, topk_ids, topk_w, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 
@@ -343,7 +383,8 @@ def routed_moe_per_tensor(xq, x_sf, topk_ids, topk_w, weights: PreparedWeights, 
         _ptr(xq), _ptr(x_sf), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1,
         expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes),
         _ptr(W.w2_scales), _ptr(W.w2_alpha), _ptr(_f32_scalar(a2)), act, _ptr(workspace),
-        workspace.numel(), _ptr(out), _stream(stream)))
+        workspace.numel(), _ptr(out),
+        _stream(stream, xq, x_sf, topk_ids, topk_w, a2, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 
@@ -359,16 +400,18 @@ def routed_moe_w4a16(x, topk_ids, topk_w, weights: PreparedWeights, act=None, ex
     _check(lib().pmoe_routed_moe_w4a16(
         _ptr(x), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1, expert_offset,
         _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes), _ptr(W.w2_scales),
-        _ptr(W.w2_alpha), act, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+        _ptr(W.w2_alpha), act, _ptr(workspace), workspace.numel(), _ptr(out),
+        _stream(stream, x, topk_ids, topk_w, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 
 def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, recipe="per_token",
                   finalize="ordered", swiglu_limit=0.0, a2=None, act=None, expert_offset=0,
-                  workspace=None, out=None, stream=None, streams=0):
+                  workspace=None, out=None, stream=None, streams=0, step_events=None):
     """The routed path with options (pmoe_routed_moe_ex): recipe "per_token" (x = xq, x_sf,
     x_scale), "per_tensor" (x = xq, x_sf; a2) or "w4a16" (x = BF16 activations; x_sf, x_scale
-    None); finalize "ordered" or "fused"; swiglu_limit > 0 clamps SwiGLU."""
+    None); finalize "ordered" or "fused"; swiglu_limit > 0 clamps SwiGLU; step_events: None
+    or STEP_EVENTS torch.cuda.Events (timing enabled) recorded around the grouped GEMMs."""
     T, K = topk_ids.shape
     W = weights
     act = W.act if act is None else act
@@ -376,35 +419,41 @@ def routed_moe_ex(x, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, 
     if recipe == "w4a16":
         x = _bf16_storage(x.contiguous())
     workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
+    evs = _event_array(step_events)
     opt = MoeOptions(_RECIPES[recipe], _FINALIZE[finalize], float(swiglu_limit),
-                     _f32_scalar(a2).data_ptr() if a2 is not None else None, int(streams))
+                     _f32_scalar(a2).data_ptr() if a2 is not None else None, int(streams), None,
+                     ctypes.cast(evs, ctypes.c_void_p) if evs is not None else None)
     _check(lib().pmoe_routed_moe_ex(
         _ptr(x), _ptr(x_sf), _ptr(x_scale), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H,
         W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
         _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, ctypes.byref(opt),
-        _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+        _ptr(workspace), workspace.numel(), _ptr(out),
+        _stream(stream, x, x_sf, x_scale, topk_ids, topk_w, a2, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 
 def moe_forward(x, topk_ids, topk_w, weights: PreparedWeights, recipe="per_token",
                 finalize="ordered", swiglu_limit=0.0, a1=None, a2=None, act=None, expert_offset=0,
-                workspace=None, out=None, stream=None, streams=0):
+                workspace=None, out=None, stream=None, streams=0, step_events=None):
     """The whole routed layer from BF16 activations x [T, H] (pmoe_moe_forward): the NVFP4
-    recipes quantize x inside the call, overlapped with the routing."""
+    recipes quantize x inside the call, overlapped with the routing. step_events: None or
+    STEP_EVENTS torch.cuda.Events (timing enabled) recorded around the grouped GEMMs."""
     T, K = topk_ids.shape
     W = weights
     act = W.act if act is None else act
     x = _bf16_storage(x.contiguous())
     topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
     workspace, out = _moe_buffers(T, K, W, act, x.device, workspace, out)
+    evs = _event_array(step_events)
     opt = MoeOptions(_RECIPES[recipe], _FINALIZE[finalize], float(swiglu_limit),
                      _f32_scalar(a2).data_ptr() if a2 is not None else None, int(streams),
-                     _f32_scalar(a1).data_ptr() if a1 is not None else None)
+                     _f32_scalar(a1).data_ptr() if a1 is not None else None,
+                     ctypes.cast(evs, ctypes.c_void_p) if evs is not None else None)
     _check(lib().pmoe_moe_forward(
         _ptr(x), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H, W.I, W.N1, expert_offset,
         _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha), _ptr(W.w2_codes), _ptr(W.w2_scales),
         _ptr(W.w2_alpha), act, ctypes.byref(opt), _ptr(workspace), workspace.numel(), _ptr(out),
-        _stream(stream)))
+        _stream(stream, x, topk_ids, topk_w, a1, a2, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 
@@ -420,7 +469,7 @@ def router_topk(logits, k, renormalize=False, out=None, stream=None):
                torch.empty((T, k), dtype=torch.float32, device=logits.device))
     ids, w = out
     _check(lib().pmoe_router_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
-                                  _stream(stream)))
+                                  _stream(stream, logits, ids, w)))
     return ids, w
 
 
@@ -432,6 +481,8 @@ def finalize(z, row_of_route, topk_w, out=None, stream=None):
     z = _bf16_storage(z.contiguous())
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=z.device)
-    _check(lib().pmoe_finalize(_ptr(z), _ptr(row_of_route.contiguous()), _ptr(topk_w.contiguous()),
-                               T, K, H, _ptr(out), _stream(stream)))
+    row_of_route = row_of_route.contiguous()
+    topk_w = topk_w.contiguous()
+    _check(lib().pmoe_finalize(_ptr(z), _ptr(row_of_route), _ptr(topk_w), T, K, H, _ptr(out),
+                               _stream(stream, z, row_of_route, topk_w, out)))
     return out

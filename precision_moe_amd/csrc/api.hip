@@ -6,6 +6,7 @@
 // for data or synchronizes with the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -83,12 +84,17 @@ int check_ptr(const void* p, size_t align, const char* name) {
   } while (0)
 
 // ------------------------------------------------------------------ shapes
-bool dim_ok(int v) { return v > 0 && v % kChunk == 0 && v <= kMaxRow; }
+// H and I: multiples of 16 (one E4M3 block) up to 16384. The grouped GEMMs
+// reduce over whole chunks of 64; a length that is not a multiple of 64 is
+// padded inside the library with zero codes and zero block scales, which add
+// exactly zero to every sum.
+bool dim_ok(int v) { return v > 0 && v % kDimStep == 0 && v <= kMaxRow; }
+#define PMOE_DIM_RULE " must be a multiple of 16 in [16, 16384]"
 
 int check_weight_shape(int E, int N1, int H, int I) {
   if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
-  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H" PMOE_DIM_RULE);
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I" PMOE_DIM_RULE);
   if (N1 != I && N1 != 2 * I)
     return fail(PMOE_ERR_SHAPE, "FC1 width N1 must be I (squared ReLU) or 2*I (SwiGLU)");
   return PMOE_OK;
@@ -99,13 +105,15 @@ struct WeightBytes {
 };
 WeightBytes weight_bytes(int E, int N1, int H, int I) {
   WeightBytes b;
-  // row counts padded to whole column tiles (8 blocks of 32 rows)
-  const size_t n1p = (size_t)padded_col_blocks(N1 / kColBlock) * kColBlock;
-  const size_t hp = (size_t)padded_col_blocks(H / kColBlock) * kColBlock;
-  b.w1q = (size_t)E * n1p * H / 2;
-  b.w1s = (size_t)E * n1p * H / 16;
-  b.w2q = (size_t)E * hp * I / 2;
-  b.w2s = (size_t)E * hp * I / 16;
+  // row counts padded to whole column tiles (8 blocks of 32 rows), reduction
+  // lengths to whole chunks of 64
+  const size_t n1p = (size_t)padded_col_blocks(col_blocks(N1, N1 == 2 * I ? I : 0)) * kColBlock;
+  const size_t hp = (size_t)padded_col_blocks(col_blocks(H, 0)) * kColBlock;
+  const size_t Hp = padded_k(H), Ip = padded_k(I);
+  b.w1q = (size_t)E * n1p * Hp / 2;
+  b.w1s = (size_t)E * n1p * Hp / 16;
+  b.w2q = (size_t)E * hp * Ip / 2;
+  b.w2s = (size_t)E * hp * Ip / 16;
   return b;
 }
 
@@ -117,7 +125,7 @@ size_t prepare_ws(int E, int N1, int H, int I) {
 // routed_moe workspace layout
 struct MoeLayout {
   size_t off[PMOE_WS_NUM_FIELDS];
-  size_t rank_local, block_counts, tiles, acc32, xq, x_sf, x_scale;
+  size_t rank_local, block_counts, tiles, acc32, xq, x_sf, x_scale, xpad;
   size_t total;
   int max_tiles;
 };
@@ -125,6 +133,7 @@ struct MoeLayout {
 MoeLayout moe_layout(int T, int K, int E, int H, int I) {
   MoeLayout L;
   const size_t TK = (size_t)T * K;
+  const size_t Hp = padded_k(H), Ip = padded_k(I);
   L.max_tiles = (int)((TK + kTileM - 1) / kTileM) + E;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -136,18 +145,21 @@ MoeLayout moe_layout(int T, int K, int E, int H, int I) {
   L.off[PMOE_WS_ROUTE_OF_ROW] = take(TK * 4);
   L.off[PMOE_WS_EXPERT_OFFSETS] = take((size_t)(E + 1) * 4);
   L.off[PMOE_WS_COUNTERS] = take(16);
-  L.off[PMOE_WS_H] = take(TK * I * 4);
-  L.off[PMOE_WS_HQ] = take(TK * I / 2);
-  L.off[PMOE_WS_H_SF] = take(TK * I / 16);
+  // FP32 h [TK, I], or BF16 h [TK, Ip] under W4A16 (FC2's A operand)
+  L.off[PMOE_WS_H] = take(std::max(TK * I * 4, TK * Ip * 2));
+  L.off[PMOE_WS_HQ] = take(TK * Ip / 2);
+  L.off[PMOE_WS_H_SF] = take(TK * Ip / 16);
   L.off[PMOE_WS_H_SCALE] = take(TK * 4);
   L.off[PMOE_WS_Z] = take(TK * H * 2);
   L.rank_local = take(TK * 4);
   L.block_counts = take((size_t)route_blocks((int)TK) * E * 4);
   L.tiles = take((size_t)L.max_tiles * 4 * 4);
   L.acc32 = take((size_t)T * H * 4);
-  L.xq = take((size_t)T * H / 2);
-  L.x_sf = take((size_t)T * H / 16);
+  L.xq = take((size_t)T * Hp / 2);
+  L.x_sf = take((size_t)T * Hp / 16);
   L.x_scale = take((size_t)T * 4);
+  // BF16 activations re-laid with padded rows (W4A16 when H is not a multiple of 64)
+  L.xpad = take(Hp == (size_t)H ? 0 : (size_t)T * Hp * 2);
   L.total = o;
   return L;
 }
@@ -156,11 +168,11 @@ int check_moe_shape(int T, int K, int E, int H, int I, int act) {
   if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
   if (E < 1 || E > kMaxExperts) return fail(PMOE_ERR_SHAPE, "E must be in [1, 1024]");
   if (K < 1 || K > 32 || K > E) return fail(PMOE_ERR_SHAPE, "K must be in [1, min(32, E)]");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
-  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H" PMOE_DIM_RULE);
+  if (!dim_ok(I)) return fail(PMOE_ERR_SHAPE, "I" PMOE_DIM_RULE);
   if ((long long)T * K >= (1LL << 31) / 2) return fail(PMOE_ERR_SHAPE, "T*K too large");
-  if ((long long)T * H >= (1LL << 31) || (long long)T * K * I >= (1LL << 31))
-    return fail(PMOE_ERR_SHAPE, "T*H and T*K*I must stay below 2^31 elements");
+  if ((long long)T * padded_k(H) >= (1LL << 31) || (long long)T * K * padded_k(I) >= (1LL << 31))
+    return fail(PMOE_ERR_SHAPE, "T*H and T*K*I (H, I rounded up to 64) must stay below 2^31 elements");
   if (act != PMOE_ACT_RELU2 && act != PMOE_ACT_SWIGLU) return fail(PMOE_ERR_ACT, "unknown activation kind");
   return PMOE_OK;
 }
@@ -169,7 +181,7 @@ int check_moe_shape(int T, int K, int E, int H, int I, int act) {
 
 // ================================================================== exports
 
-PMOE_EXPORT int pmoe_version(void) { return 100; }
+PMOE_EXPORT int pmoe_version(void) { return 200; }
 
 PMOE_EXPORT const char* pmoe_last_error(void) { return g_last_error.c_str(); }
 
@@ -252,14 +264,14 @@ PMOE_EXPORT int pmoe_prepare_weights_per_tensor(const void* w1, const void* w2, 
 PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void* xq, void* x_sf,
                                               float* x_scale, void* stream) {
   if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H" PMOE_DIM_RULE);
   if (T == 0) return ok();
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(x, 16, "x"));
   PMOE_TRY(check_ptr(xq, 16, "xq"));
   PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
   PMOE_TRY(check_ptr(x_scale, 4, "x_scale"));
-  PMOE_HIP(launch_quantize_bf16(x, T, H, nullptr, static_cast<uint8_t*>(xq),
+  PMOE_HIP(launch_quantize_bf16(x, T, H, H, nullptr, static_cast<uint8_t*>(xq),
                                 static_cast<uint8_t*>(x_sf), x_scale,
                                 static_cast<hipStream_t>(stream)));
   return ok();
@@ -268,14 +280,14 @@ PMOE_EXPORT int pmoe_quantize_input_per_token(const void* x, int T, int H, void*
 PMOE_EXPORT int pmoe_quantize_input_per_tensor(const void* x, int T, int H, const float* a1_scale,
                                                void* xq, void* x_sf, void* stream) {
   if (T < 0) return fail(PMOE_ERR_SHAPE, "T must be >= 0");
-  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(H)) return fail(PMOE_ERR_SHAPE, "H" PMOE_DIM_RULE);
   if (T == 0) return ok();
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(x, 16, "x"));
   PMOE_TRY(check_ptr(a1_scale, 4, "a1_scale"));
   PMOE_TRY(check_ptr(xq, 16, "xq"));
   PMOE_TRY(check_ptr(x_sf, 4, "x_sf"));
-  PMOE_HIP(launch_quantize_bf16(x, T, H, a1_scale, static_cast<uint8_t*>(xq),
+  PMOE_HIP(launch_quantize_bf16(x, T, H, H, a1_scale, static_cast<uint8_t*>(xq),
                                 static_cast<uint8_t*>(x_sf), nullptr,
                                 static_cast<hipStream_t>(stream)));
   return ok();
@@ -284,14 +296,14 @@ PMOE_EXPORT int pmoe_quantize_input_per_tensor(const void* x, int T, int H, cons
 PMOE_EXPORT int pmoe_quantize_rows_f32(const float* h, int R, int L, void* hq, void* h_sf,
                                        float* h_scale, void* stream) {
   if (R < 0) return fail(PMOE_ERR_SHAPE, "R must be >= 0");
-  if (!dim_ok(L)) return fail(PMOE_ERR_SHAPE, "L must be a multiple of 64 in [64, 16384]");
+  if (!dim_ok(L)) return fail(PMOE_ERR_SHAPE, "L" PMOE_DIM_RULE);
   if (R == 0) return ok();
   PMOE_TRY(check_device());
   PMOE_TRY(check_ptr(h, 16, "h"));
   PMOE_TRY(check_ptr(hq, 16, "hq"));
   PMOE_TRY(check_ptr(h_sf, 4, "h_sf"));
   PMOE_TRY(check_ptr(h_scale, 4, "h_scale"));
-  PMOE_HIP(launch_quantize_f32(h, R, nullptr, nullptr, L, nullptr, static_cast<uint8_t*>(hq),
+  PMOE_HIP(launch_quantize_f32(h, R, nullptr, nullptr, L, L, nullptr, static_cast<uint8_t*>(hq),
                                static_cast<uint8_t*>(h_sf), h_scale, false,
                                static_cast<hipStream_t>(stream)));
   return ok();
@@ -333,6 +345,26 @@ struct Aux {
 std::mutex g_aux_mu;
 Aux g_aux[64];
 
+// True when the second stream may join this call: it is idle with respect to
+// graph capture, or it is already part of the capture the caller's stream is
+// in (a second call inside the same capture). A second stream held by another
+// caller's capture would pull this call's kernels into that graph, so the
+// call then runs on the caller's stream alone. Call with g_aux_mu held.
+bool aux_usable(const Aux& a, hipStream_t s) {
+  hipStreamCaptureStatus st2 = hipStreamCaptureStatusNone, st = hipStreamCaptureStatusNone;
+  unsigned long long id2 = 0, id = 0;
+  if (hipStreamGetCaptureInfo(a.s2, &st2, &id2) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (st2 == hipStreamCaptureStatusNone) return true;
+  if (hipStreamGetCaptureInfo(s, &st, &id) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return st == hipStreamCaptureStatusActive && st2 == hipStreamCaptureStatusActive && id == id2;
+}
+
 // The current device's Aux, created on first use. Call with g_aux_mu held.
 // Either all four objects exist afterwards or none is kept (a failed
 // creation is reported and retried on the next call).
@@ -373,7 +405,8 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
              const void* w1_scales, const float* w1_alpha, const void* w2_codes,
              const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
              void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f,
-             int streams = 0, bool bf16_input = false, const float* a1 = nullptr) {
+             int streams = 0, bool bf16_input = false, const float* a1 = nullptr,
+             void* const* step_events = nullptr) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
   if (!(swiglu_limit >= 0.0f)) return fail(PMOE_ERR_ARG, "swiglu_limit must be >= 0");
@@ -384,6 +417,9 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
                                                       : "squared ReLU needs a non-gated FC1 (N1 == I)");
   if (ids_type != PMOE_IDS_INT32 && ids_type != PMOE_IDS_INT64)
     return fail(PMOE_ERR_ARG, "ids_type must be PMOE_IDS_INT32 or PMOE_IDS_INT64");
+  const int Hp = padded_k(H), Ip = padded_k(I);
+  if (rc == kW4A16 && (2LL * T * Hp >= (1LL << 31) || 2LL * T * K * Ip >= (1LL << 31)))
+    return fail(PMOE_ERR_SHAPE, "W4A16: 2*T*H and 2*T*K*I (H, I rounded up to 64) must stay below 2^31");
   if (T == 0) return ok();
   PMOE_TRY(check_device());
   if (bf16_input && (first != PMOE_STEP_ROUTE || last != PMOE_STEP_FINALIZE))
@@ -428,8 +464,8 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   const bool quant_in = bf16_input && rc != kW4A16;
   // Two streams for the whole FC1..FC2 range when asked (streams == 2) or by
   // default (streams == 0) once there is enough work to fill the GPU twice.
-  const bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
-                     (streams == 2 || (streams == 0 && TK >= 2048));
+  bool split = first <= PMOE_STEP_FC1 && last >= PMOE_STEP_FC2 && E >= 2 &&
+               (streams == 2 || (streams == 0 && TK >= 2048));
   // One lock for the whole enqueue when the second stream is used, so that the
   // record / wait pairs of concurrent host threads do not interleave.
   std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
@@ -437,7 +473,15 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   if ((quant_in && !route_quantize_fits(TK)) || split) {
     lock.lock();
     PMOE_TRY(aux_for_current_device(&aux));
+    if (!aux_usable(*aux, s)) {  // captured elsewhere: everything on the caller's stream
+      aux = nullptr;
+      split = false;
+    }
   }
+  auto record = [&](int i, hipStream_t st) -> int {
+    if (step_events && step_events[i]) PMOE_HIP(hipEventRecord(static_cast<hipEvent_t>(step_events[i]), st));
+    return PMOE_OK;
+  };
   bool s2_after_route = false;  // the second stream already follows the routing
   if (quant_in && route_quantize_fits(TK)) {
     // route and quantize the BF16 activations in one launch on the caller's
@@ -446,7 +490,18 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
     float* wsc = reinterpret_cast<float*>(base + L.x_scale);
     PMOE_HIP(launch_route_quantize(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, x,
-                                   T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, s));
+                                   T, H, Hp, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, s));
+    if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+    x = wq;
+    x_sf = wsf;
+    x_scale = rc == kPerToken ? wsc : nullptr;
+  } else if (quant_in && !aux) {
+    // the second stream is not available: quantize, then route, on the caller's stream
+    uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
+    uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
+    float* wsc = reinterpret_cast<float*>(base + L.x_scale);
+    PMOE_HIP(launch_quantize_bf16(x, T, H, Hp, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, s));
+    PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
     if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
     x = wq;
     x_sf = wsf;
@@ -459,7 +514,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     float* wsc = reinterpret_cast<float*>(base + L.x_scale);
     PMOE_HIP(hipEventRecord(aux->fork, s));
     PMOE_HIP(hipStreamWaitEvent(aux->s2, aux->fork, 0));
-    PMOE_HIP(launch_quantize_bf16(x, T, H, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, aux->s2));
+    PMOE_HIP(launch_quantize_bf16(x, T, H, Hp, rc == kPerTensor ? a1 : nullptr, wq, wsf, wsc, aux->s2));
     PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
     if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
     if (split) {
@@ -476,6 +531,21 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     if (run(PMOE_STEP_ROUTE))
       PMOE_HIP(launch_route(topk_ids, ids_type == PMOE_IDS_INT64, TK, E, expert_offset, rb, s));
     if (fill_acc) PMOE_HIP(launch_fill_zero(acc32, (long)T * H, s));
+    if (Hp != H && run(PMOE_STEP_FC1)) {
+      // canonical FC1 input rows re-laid with zero-padded rows of Hp elements
+      if (rc == kW4A16) {
+        void* xp = base + L.xpad;
+        PMOE_HIP(launch_pad_rows(x, T, 2L * H, 2L * Hp, xp, s));
+        x = xp;
+      } else {
+        uint8_t* wq = reinterpret_cast<uint8_t*>(base + L.xq);
+        uint8_t* wsf = reinterpret_cast<uint8_t*>(base + L.x_sf);
+        PMOE_HIP(launch_pad_rows(x, T, H / 2, Hp / 2, wq, s));
+        PMOE_HIP(launch_pad_rows(x_sf, T, H / 16, Hp / 16, wsf, s));
+        x = wq;
+        x_sf = wsf;
+      }
+    }
   }
 
   void* h = base + L.off[PMOE_WS_H];  // FP32 h, or BF16 h under W4A16
@@ -496,13 +566,16 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p1.w_codes = static_cast<const uint8_t*>(w1_codes);
   p1.w_scales = static_cast<const uint8_t*>(w1_scales);
   p1.w_alpha = w1_alpha;
-  p1.NB = N1 / kColBlock;
-  p1.KC = H / kChunk;
+  p1.NB = col_blocks(N1, act == PMOE_ACT_SWIGLU ? I : 0);
+  p1.KC = Hp / kChunk;
   p1.tiles = rb.tiles;
   p1.counters = rb.counters;
   p1.max_tiles = L.max_tiles;
   p1.out = h;
-  p1.out_stride = I;
+  // FP32 h keeps canonical rows for the requant; BF16 h (W4A16) is FC2's A
+  // operand, so its rows are padded to Ip (the padding columns compute to 0)
+  p1.out_stride = bf16_a ? Ip : I;
+  p1.n_out = bf16_a ? Ip : I;
   p1.swiglu_limit = swiglu_limit;
   p1.out_route = nullptr;
   p1.out_w = nullptr;
@@ -517,10 +590,11 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   p2.w_codes = static_cast<const uint8_t*>(w2_codes);
   p2.w_scales = static_cast<const uint8_t*>(w2_scales);
   p2.w_alpha = w2_alpha;
-  p2.NB = H / kColBlock;
-  p2.KC = I / kChunk;
+  p2.NB = col_blocks(H, 0);
+  p2.KC = Ip / kChunk;
   p2.out = z;
   p2.out_stride = H;
+  p2.n_out = H;
   if (fused) {
     p2.out = acc32;
     p2.out_route = rb.route_of_row;
@@ -536,11 +610,26 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
     q1.part = q2.part = part;
     const int* row_begin = part == 2 ? rb.counters + 3 : nullptr;
     const int* row_end = part == 1 ? rb.counters + 3 : rb.counters;
-    if (fc1) PMOE_HIP(launch_fc(m1, q1, st));
+    // timing events: part 1 (or the whole set) at 0, 1 (FC1) and 4, 5 (FC2);
+    // part 2 at 2, 3 and 6, 7; one part alone records both pairs
+    const int e0 = part == 2 ? 2 : 0;
+    if (fc1) {
+      PMOE_TRY(record(e0, st));
+      if (part == 0) PMOE_TRY(record(2, st));
+      PMOE_HIP(launch_fc(m1, q1, st));
+      PMOE_TRY(record(e0 + 1, st));
+      if (part == 0) PMOE_TRY(record(3, st));
+    }
     if (requant && rc != kW4A16)
-      PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, row_begin, row_end, I,
+      PMOE_HIP(launch_quantize_f32(static_cast<const float*>(h), TK, row_begin, row_end, I, Ip,
                                    static_a2, hq, h_sf, h_scale, part != 0, st));
-    if (fc2) PMOE_HIP(launch_fc(m2, q2, st));
+    if (fc2) {
+      PMOE_TRY(record(e0 + 4, st));
+      if (part == 0) PMOE_TRY(record(6, st));
+      PMOE_HIP(launch_fc(m2, q2, st));
+      PMOE_TRY(record(e0 + 5, st));
+      if (part == 0) PMOE_TRY(record(7, st));
+    }
     return PMOE_OK;
   };
   if (split) {
@@ -612,7 +701,7 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
                                    const void* w2_scales, const float* w2_alpha, int act,
                                    const pmoe_moe_options* options, void* ws, size_t ws_bytes,
                                    void* out, void* stream) {
-  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr};
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr, nullptr};
   if (options) o = *options;
   if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
       o.recipe != PMOE_RECIPE_W4A16)
@@ -630,7 +719,7 @@ PMOE_EXPORT int pmoe_routed_moe_ex(const void* x, const void* x_sf, const float*
                   rc == kPerToken ? x_scale : nullptr, o.a2_scale, topk_ids, ids_type, topk_w, T, K,
                   E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha, w2_codes, w2_scales,
                   w2_alpha, act, ws, ws_bytes, out, stream, o.finalize == PMOE_FINALIZE_FUSED,
-                  o.swiglu_limit, o.streams);
+                  o.swiglu_limit, o.streams, false, nullptr, o.step_events);
 }
 
 PMOE_EXPORT int pmoe_moe_forward(const void* x, const void* topk_ids, int ids_type,
@@ -640,7 +729,7 @@ PMOE_EXPORT int pmoe_moe_forward(const void* x, const void* topk_ids, int ids_ty
                                  const void* w2_scales, const float* w2_alpha, int act,
                                  const pmoe_moe_options* options, void* ws, size_t ws_bytes,
                                  void* out, void* stream) {
-  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr};
+  pmoe_moe_options o = {PMOE_RECIPE_PER_TOKEN, PMOE_FINALIZE_ORDERED, 0.0f, nullptr, 0, nullptr, nullptr};
   if (options) o = *options;
   if (o.recipe != PMOE_RECIPE_PER_TOKEN && o.recipe != PMOE_RECIPE_PER_TENSOR &&
       o.recipe != PMOE_RECIPE_W4A16)
@@ -656,7 +745,8 @@ PMOE_EXPORT int pmoe_moe_forward(const void* x, const void* topk_ids, int ids_ty
   return moe_path(rc, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, x, nullptr, nullptr, o.a2_scale, topk_ids,
                   ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha,
                   w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream,
-                  o.finalize == PMOE_FINALIZE_FUSED, o.swiglu_limit, o.streams, true, o.a1_scale);
+                  o.finalize == PMOE_FINALIZE_FUSED, o.swiglu_limit, o.streams, true, o.a1_scale,
+                  o.step_events);
 }
 
 PMOE_EXPORT int pmoe_router_topk(const float* logits, int T, int E, int K, int renormalize,

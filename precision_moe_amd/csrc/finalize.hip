@@ -56,7 +56,7 @@ hipError_t launch_finalize(const uint16_t* z, const int* row_of_route, const flo
 // atomic adds inside FC2 (the non-deterministic mode the two-stage finalize
 // replaces); these two kernels clear the accumulator before FC2 and round it
 // to BF16 after. A plain fill kernel rather than a memset keeps the sequence
-// safe to capture in a graph. n is a multiple of 8 (H is a multiple of 64).
+// safe to capture in a graph. n is a multiple of 8 (H is a multiple of 16).
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long n4) {
   for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
     p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

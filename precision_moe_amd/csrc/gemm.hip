@@ -326,8 +326,9 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   // stores below reuse.
   __syncthreads();
   // acc[rb][cb][i] is row 16*rb + 4*(lane/16) + i, column 16*cb + lane%16 of
-  // the wave's 64 columns: position p0 + cb/2, half h = cb%2.
-  const bool use0 = p0 < NB, use1 = p0 + 1 < NB;
+  // the wave's 64 columns: position p0 + cb/2, half h = cb%2. Only output
+  // columns below P.n_out are written (padding positions and the zero rows
+  // that pad a partial column block are dropped; P.n_out is a multiple of 16).
   const int n16 = lane & 15;
   if constexpr (MODE == kFc2Fused) {
 #pragma unroll
@@ -344,8 +345,8 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
-          if (use0) unsafeAtomicAdd(acc_row + col0, wgt * (acc[rb][h][i] * s));
-          if (use1) unsafeAtomicAdd(acc_row + col1, wgt * (acc[rb][2 + h][i] * s));
+          if (col0 < P.n_out) unsafeAtomicAdd(acc_row + col0, wgt * (acc[rb][h][i] * s));
+          if (col1 < P.n_out) unsafeAtomicAdd(acc_row + col1, wgt * (acc[rb][2 + h][i] * s));
         }
       }
     }
@@ -362,9 +363,9 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     constexpr int kRowB = kCw * kS;                                 // LDS bytes per row
     constexpr int kPassRows = (8192 / kRowB) < kTileM ? 8192 / kRowB : kTileM;
     uint8_t* wbuf = &a_lds[0][0] + wave * 8192;
-    const long col_base = kSwiglu ? (long)kColBlock * (p0 >> 1) : (long)kColBlock * p0;
-    // bytes of an LDS row that exist in the output: padding positions past NB are dropped
-    const int row_bytes = kSwiglu ? (use0 ? kRowB : 0) : (use1 ? kRowB : (use0 ? kRowB / 2 : 0));
+    const int col_base = kSwiglu ? kColBlock * (p0 >> 1) : kColBlock * p0;
+    // bytes of an LDS row that exist in the output (whole 16-byte pieces)
+    const int row_bytes = min(max(P.n_out - col_base, 0), kCw) * kS;
     auto put = [&](int m, int lc, float v) {
       if constexpr (kS == 2)
         *reinterpret_cast<uint16_t*>(wbuf + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(v);
@@ -411,7 +412,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
       }
       __syncthreads();
       const int nrow = min(kPassRows, mrows - r_lo);
-      uint8_t* out = static_cast<uint8_t*>(P.out) + ((long)(row0 + r_lo) * P.out_stride + col_base) * kS;
+      uint8_t* out = static_cast<uint8_t*>(P.out) + ((long)(row0 + r_lo) * P.out_stride + (long)col_base) * kS;
 #pragma unroll
       for (int k = 0; k < kPassRows * kRowB / (64 * 16); ++k) {
         const int off = (k * 64 + lane) * 16;

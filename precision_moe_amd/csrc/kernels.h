@@ -16,18 +16,33 @@ __host__ __device__ inline int padded_col_blocks(int NB) {
 constexpr int kRouteBlock = 256;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxRow = 16384;  // longest row (H, I) the path accepts
+constexpr int kDimStep = 16;    // H and I are multiples of this (one E4M3 block)
+// A reduction length padded to whole GEMM chunks: the operands of the grouped
+// GEMMs carry zero codes and zero scales in [Kd, padded_k(Kd)).
+__host__ __device__ inline int padded_k(int Kd) { return (Kd + kChunk - 1) / kChunk * kChunk; }
+// Prepared column blocks of an FC matrix with N output rows; a gated FC1
+// (N = 2I) has ceil(I/32) gate blocks and as many up blocks, interleaved.
+__host__ __device__ inline int col_blocks(int N, int gated_I) {
+  return gated_I > 0 ? 2 * ((gated_I + kColBlock - 1) / kColBlock) : (N + kColBlock - 1) / kColBlock;
+}
 
 // ---------------------------------------------------------------- quantizers
 // static_a: null for per-row scales (written to *_scale), else the device
 // address of a static scale a (rows use g = 1/a; no scale is written).
-hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
-                                uint8_t* x_sf, float* x_scale, hipStream_t s);
+// Input rows have H (L) elements; output rows Hq (Lq) >= H, the blocks past H
+// written as zeros.
+hipError_t launch_quantize_bf16(const void* x, int T, int H, int Hq, const float* static_a,
+                                uint8_t* xq, uint8_t* x_sf, float* x_scale, hipStream_t s);
 // Rows [*row_begin_dev, *row_end_dev) of R (either pointer may be null: 0 / R).
 // beside_gemm: the launch runs while another stream's grouped GEMM holds the
 // CUs (one wave per row over a bounded grid); else one workgroup per row.
 hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
-                               const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, bool beside_gemm, hipStream_t s);
+                               const int* row_end_dev, int L, int Lq, const float* static_a,
+                               uint8_t* hq, uint8_t* h_sf, float* h_scale, bool beside_gemm,
+                               hipStream_t s);
+// rows x row_bytes -> rows x dst_row_bytes, the tail of every row zero-filled.
+hipError_t launch_pad_rows(const void* src, long rows, long row_bytes, long dst_row_bytes, void* dst,
+                           hipStream_t s);
 
 // ---------------------------------------------------------------- weights
 int weight_amax_parts(long elems);
@@ -55,7 +70,7 @@ hipError_t launch_route(const void* ids, bool ids64, int TK, int E, int expert_o
 // (route_quantize_fits); same results as launch_route + launch_quantize_bf16.
 bool route_quantize_fits(int TK);
 hipError_t launch_route_quantize(const void* ids, bool ids64, int TK, int E, int expert_offset,
-                                 const RouteBuffers& b, const void* x, int T, int H,
+                                 const RouteBuffers& b, const void* x, int T, int H, int Hq,
                                  const float* static_a, uint8_t* xq, uint8_t* x_sf, float* x_scale,
                                  hipStream_t s);
 
@@ -73,8 +88,9 @@ struct FcParams {
   const uint8_t* w_codes;    // prepared layout
   const uint8_t* w_scales;
   const float* w_alpha;
-  int NB;                    // column blocks of 32 in this FC
-  int KC;                    // chunks of 64 along the reduction
+  int NB;                    // column blocks of 32 in this FC (before padding to whole tiles)
+  int KC;                    // chunks of 64 along the (padded) reduction
+  int n_out;                 // output columns written (FC1 SwiGLU: of the activation output)
   const int* tiles;          // [tiles][4], see RouteBuffers
   const int* counters;       // [1] = number of M-tiles, [2] = first M-tile of the second part
   int part;                  // 0: all tiles; 1 / 2: the tiles before / from counters[2]

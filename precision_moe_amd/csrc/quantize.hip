@@ -31,7 +31,8 @@ template <bool kBf16, bool kStatic>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int rows,
                                                             const int* __restrict__ row_begin_dev,
                                                             const int* __restrict__ row_end_dev,
-                                                            int L, const float* __restrict__ static_a,
+                                                            int L, int Lq,
+                                                            const float* __restrict__ static_a,
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             float* __restrict__ scale) {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
   const long row = blockIdx.x + (row_begin_dev ? *row_begin_dev : 0);
   const int nrows = row_end_dev ? *row_end_dev : rows;
   if (row >= nrows) return;  // uniform across the workgroup
-  quantize_row_group<kBf16, kStatic>(x, row, true, L, threadIdx.x, static_a, q, sf, scale, red);
+  quantize_row_group<kBf16, kStatic>(x, row, true, L, Lq, threadIdx.x, static_a, q, sf, scale, red);
 }
 
 // Wave w of workgroup b takes rows begin + 4b + w, then every 4 * gridDim.x
@@ -47,13 +48,13 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 template <bool kBf16, bool kStatic>
 __global__ __launch_bounds__(256) void quantize_rows_loop_kernel(
     const void* __restrict__ x, int rows, const int* __restrict__ row_begin_dev,
-    const int* __restrict__ row_end_dev, int L, const float* __restrict__ static_a,
+    const int* __restrict__ row_end_dev, int L, int Lq, const float* __restrict__ static_a,
     uint8_t* __restrict__ q, uint8_t* __restrict__ sf, float* __restrict__ scale) {
   const long begin = row_begin_dev ? *row_begin_dev : 0;
   const long end = row_end_dev ? *row_end_dev : rows;
   const long step = (long)gridDim.x * 4;
   for (long row = begin + (long)blockIdx.x * 4 + (threadIdx.x >> 6); row < end; row += step)
-    quantize_row_wave<kBf16, kStatic>(x, row, L, threadIdx.x & 63, static_a, q, sf, scale);
+    quantize_row_wave<kBf16, kStatic>(x, row, L, Lq, threadIdx.x & 63, static_a, q, sf, scale);
 }
 
 // At most kLoopGroups workgroups of four waves for the looping kernel.
@@ -63,34 +64,73 @@ static int loop_grid(int rows) {
   return g < 1 ? 1 : (g < kLoopGroups ? g : kLoopGroups);
 }
 
-hipError_t launch_quantize_bf16(const void* x, int T, int H, const float* static_a, uint8_t* xq,
-                                uint8_t* x_sf, float* x_scale, hipStream_t s) {
+hipError_t launch_quantize_bf16(const void* x, int T, int H, int Hq, const float* static_a,
+                                uint8_t* xq, uint8_t* x_sf, float* x_scale, hipStream_t s) {
   if (static_a)
-    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, static_a, xq, x_sf,
-                                                       nullptr);
+    quantize_rows_kernel<true, true><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, Hq, static_a, xq,
+                                                       x_sf, nullptr);
   else
-    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, nullptr, xq, x_sf,
-                                                        x_scale);
+    quantize_rows_kernel<true, false><<<T, 256, 0, s>>>(x, T, nullptr, nullptr, H, Hq, nullptr, xq,
+                                                        x_sf, x_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_f32(const float* h, int R, const int* row_begin_dev,
-                               const int* row_end_dev, int L, const float* static_a, uint8_t* hq,
-                               uint8_t* h_sf, float* h_scale, bool beside_gemm, hipStream_t s) {
+                               const int* row_end_dev, int L, int Lq, const float* static_a,
+                               uint8_t* hq, uint8_t* h_sf, float* h_scale, bool beside_gemm,
+                               hipStream_t s) {
   if (beside_gemm) {
     if (static_a)
       quantize_rows_loop_kernel<false, true><<<loop_grid(R), 256, 0, s>>>(
-          h, R, row_begin_dev, row_end_dev, L, static_a, hq, h_sf, nullptr);
+          h, R, row_begin_dev, row_end_dev, L, Lq, static_a, hq, h_sf, nullptr);
     else
       quantize_rows_loop_kernel<false, false><<<loop_grid(R), 256, 0, s>>>(
-          h, R, row_begin_dev, row_end_dev, L, nullptr, hq, h_sf, h_scale);
+          h, R, row_begin_dev, row_end_dev, L, Lq, nullptr, hq, h_sf, h_scale);
   } else if (static_a) {
-    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, static_a,
-                                                        hq, h_sf, nullptr);
+    quantize_rows_kernel<false, true><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, Lq,
+                                                        static_a, hq, h_sf, nullptr);
   } else {
-    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, nullptr,
-                                                         hq, h_sf, h_scale);
+    quantize_rows_kernel<false, false><<<R, 256, 0, s>>>(h, R, row_begin_dev, row_end_dev, L, Lq,
+                                                         nullptr, hq, h_sf, h_scale);
   }
+  return hipGetLastError();
+}
+
+// Copy rows of `row_bytes` bytes into rows of `dst_row_bytes` >= row_bytes, zero-filling
+// the rest: a canonical operand whose reduction length is not a multiple of 64, laid
+// out for the grouped GEMMs (whole 64-element chunks). kW bytes per thread and step;
+// both row sizes are multiples of kW.
+template <typename W>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const W* __restrict__ src, long rows,
+                                                       int row_w, int dst_row_w,
+                                                       W* __restrict__ dst) {
+  const long n = rows * dst_row_w;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long r = i / dst_row_w;
+    const int c = (int)(i - r * dst_row_w);
+    W v;
+    if (c < row_w)
+      v = src[r * row_w + c];
+    else
+      __builtin_memset(&v, 0, sizeof(W));
+    dst[i] = v;
+  }
+}
+
+hipError_t launch_pad_rows(const void* src, long rows, long row_bytes, long dst_row_bytes, void* dst,
+                           hipStream_t s) {
+  const long n = rows * dst_row_bytes;
+  long blocks = (n / 16 + 255) / 256;
+  const int grid = (int)(blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks));
+  if (row_bytes % 16 == 0 && dst_row_bytes % 16 == 0)
+    pad_rows_kernel<uint4><<<grid, 256, 0, s>>>(static_cast<const uint4*>(src), rows, (int)(row_bytes / 16),
+                                                (int)(dst_row_bytes / 16), static_cast<uint4*>(dst));
+  else if (row_bytes % 8 == 0 && dst_row_bytes % 8 == 0)
+    pad_rows_kernel<uint2><<<grid, 256, 0, s>>>(static_cast<const uint2*>(src), rows, (int)(row_bytes / 8),
+                                                (int)(dst_row_bytes / 8), static_cast<uint2*>(dst));
+  else
+    pad_rows_kernel<uint8_t><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(src), rows, (int)row_bytes,
+                                                  (int)dst_row_bytes, static_cast<uint8_t*>(dst));
   return hipGetLastError();
 }
 

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(1024) void route_quantize_kernel(
     const IdT* __restrict__ ids, int TK, int E, int offset, int nbits,
     int* __restrict__ expert_offsets, int* __restrict__ tiles, int* __restrict__ counters,
     int* __restrict__ row_of_route, int* __restrict__ route_of_row, const void* __restrict__ x,
-    int T, int H, const float* __restrict__ static_a, uint8_t* __restrict__ xq,
+    int T, int H, int Hq, const float* __restrict__ static_a, uint8_t* __restrict__ xq,
     uint8_t* __restrict__ x_sf, float* __restrict__ x_scale) {
   __shared__ RouteSmallLds lds;
   if (blockIdx.x == 0) {
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(1024) void route_quantize_kernel(
   }
   const int grp = threadIdx.x >> 8;
   const long row = (long)(blockIdx.x - 1) * 4 + grp;
-  quantize_row_group<true, kStatic>(x, row, row < T, H, threadIdx.x & 255, static_a, xq, x_sf,
+  quantize_row_group<true, kStatic>(x, row, row < T, H, Hq, threadIdx.x & 255, static_a, xq, x_sf,
                                     x_scale, reinterpret_cast<float*>(lds.sh) + 4 * grp);
 }
 
@@ -341,30 +341,30 @@ bool route_quantize_fits(int TK) { return TK <= kRouteSmall; }
 
 template <typename IdT>
 static void launch_route_quantize_t(const IdT* ids, int TK, int E, int expert_offset,
-                                    const RouteBuffers& b, const void* x, int T, int H,
+                                    const RouteBuffers& b, const void* x, int T, int H, int Hq,
                                     const float* static_a, uint8_t* xq, uint8_t* x_sf,
                                     float* x_scale, hipStream_t s) {
   const int grid = 1 + (T + 3) / 4;
   if (static_a)
     route_quantize_kernel<IdT, true><<<grid, 1024, 0, s>>>(
         ids, TK, E, expert_offset, expert_bits(E), b.expert_offsets, b.tiles, b.counters,
-        b.row_of_route, b.route_of_row, x, T, H, static_a, xq, x_sf, nullptr);
+        b.row_of_route, b.route_of_row, x, T, H, Hq, static_a, xq, x_sf, nullptr);
   else
     route_quantize_kernel<IdT, false><<<grid, 1024, 0, s>>>(
         ids, TK, E, expert_offset, expert_bits(E), b.expert_offsets, b.tiles, b.counters,
-        b.row_of_route, b.route_of_row, x, T, H, nullptr, xq, x_sf, x_scale);
+        b.row_of_route, b.route_of_row, x, T, H, Hq, nullptr, xq, x_sf, x_scale);
 }
 
 hipError_t launch_route_quantize(const void* ids, bool ids64, int TK, int E, int expert_offset,
-                                 const RouteBuffers& b, const void* x, int T, int H,
+                                 const RouteBuffers& b, const void* x, int T, int H, int Hq,
                                  const float* static_a, uint8_t* xq, uint8_t* x_sf, float* x_scale,
                                  hipStream_t s) {
   if (!route_quantize_fits(TK)) return hipErrorInvalidValue;
   if (ids64)
     launch_route_quantize_t(static_cast<const long long*>(ids), TK, E, expert_offset, b, x, T, H,
-                            static_a, xq, x_sf, x_scale, s);
+                            Hq, static_a, xq, x_sf, x_scale, s);
   else
-    launch_route_quantize_t(static_cast<const int*>(ids), TK, E, expert_offset, b, x, T, H,
+    launch_route_quantize_t(static_cast<const int*>(ids), TK, E, expert_offset, b, x, T, H, Hq,
                             static_a, xq, x_sf, x_scale, s);
   return hipGetLastError();
 }

@@ -44,7 +44,12 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
   }
 }
 
-// Row `row` of x ([rows][L], BF16 or FP32) -> q [rows][L/2], sf [rows][L/16],
+// Output rows may be wider than the input: Lq >= L (both multiples of 16)
+// elements per output row, so q rows are Lq/2 bytes and sf rows Lq/16; the
+// blocks in [L, Lq) get zero codes and a zero scale, which is what the grouped
+// GEMMs need where a reduction is padded up to whole 64-element chunks.
+
+// Row `row` of x ([rows][L], BF16 or FP32) -> q [rows][Lq/2], sf [rows][Lq/16],
 // scale [rows] (per-row recipe), by one whole wave (lane = 0..63; every lane
 // of the wave calls it for the same row). Two passes over the row: lane l's
 // blocks are l, l+64, ...; pass 1 reads them for the row amax (a wave
@@ -52,7 +57,7 @@ __device__ __forceinline__ void load_block16(const void* row, int b, float (&x)[
 // quantizes four blocks at a time.
 template <bool kBf16, bool kStatic>
 __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, long row, int L,
-                                                  int lane, const float* __restrict__ static_a,
+                                                  int Lq, int lane, const float* __restrict__ static_a,
                                                   uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ sf,
                                                   float* __restrict__ scale) {
@@ -79,8 +84,9 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, lo
     }
     g = wave_max(amax) * kRecipeConst;
   }
-  uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
-  uint8_t* sr = sf + row * nblk;
+  const int nblk_q = Lq / kBlock;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * (Lq / 2));
+  uint8_t* sr = sf + row * nblk_q;
   for (int b0 = lane; b0 < nblk; b0 += 64 * kGroup) {
     float v[kGroup][16];
 #pragma unroll
@@ -97,6 +103,10 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, lo
       }
     }
   }
+  for (int b = nblk + lane; b < nblk_q; b += 64) {  // padding blocks
+    qr[b] = make_uint2(0u, 0u);
+    sr[b] = 0;
+  }
   if constexpr (!kStatic) {
     if (lane == 0) scale[row] = g;
   }
@@ -110,7 +120,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, lo
 // the call, and a group with no row passes active = false.
 template <bool kBf16, bool kStatic>
 __device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, long row,
-                                                   bool active, int L, int lt,
+                                                   bool active, int L, int Lq, int lt,
                                                    const float* __restrict__ static_a,
                                                    uint8_t* __restrict__ q,
                                                    uint8_t* __restrict__ sf,
@@ -143,8 +153,9 @@ __device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, l
     g = amax * kRecipeConst;
   }
   if (!active) return;
-  uint2* qr = reinterpret_cast<uint2*>(q + row * (L / 2));
-  uint8_t* sr = sf + row * nblk;
+  const int nblk_q = Lq / kBlock;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * (Lq / 2));
+  uint8_t* sr = sf + row * nblk_q;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = lt + 256 * i;
@@ -153,6 +164,9 @@ __device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, l
       const uint32_t s = quant_block16(v[i], g, lo, hi);
       qr[b] = make_uint2(lo, hi);
       sr[b] = (uint8_t)s;
+    } else if (b < nblk_q) {  // padding block
+      qr[b] = make_uint2(0u, 0u);
+      sr[b] = 0;
     }
   }
   if constexpr (!kStatic) {

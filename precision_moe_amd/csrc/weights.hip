@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __rest
 }
 
 // grid (NBp, E) with NBp = NB rounded up to a multiple of 8. gated_I > 0
-// selects the gate/up interleave of a gated FC1.
+// selects the gate/up interleave of a gated FC1. KC chunks of 64 cover Kd
+// (a multiple of 16) rounded up; blocks past Kd, rows past N (past I in each
+// half of a gated FC1) and whole padding column blocks are written as zeros.
 __global__ __launch_bounds__(256) void weight_quant_kernel(
     const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int NBp, int KC,
     const float* __restrict__ partials, int parts, const float* __restrict__ fold_a,
@@ -83,11 +85,16 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   const int tid = threadIdx.x;
   const int col = tid >> 3;  // row of the column block (0..31)
   const int bl = tid & 7;    // block of the round: chunk bl/4, block bl%4 of that chunk
-  int n;                     // canonical row (only read when p < NB)
-  if (gated_I > 0)
-    n = ((p & 1) ? gated_I : 0) + kColBlock * (p >> 1) + col;
-  else
+  int n;                     // canonical row (only read when row_ok)
+  bool row_ok;
+  if (gated_I > 0) {
+    const int r = kColBlock * (p >> 1) + col;  // row within the gate or the up half
+    n = ((p & 1) ? gated_I : 0) + r;
+    row_ok = p < NB && r < gated_I;
+  } else {
     n = kColBlock * p + col;
+    row_ok = p < NB && n < N;
+  }
   const int cs = bl >> 2, j = bl & 3;
   // block j of a chunk is half jj of k-step s; its row sits in 16-column
   // block h of the position. Lane 32*jj + col%16 holds elements 0..7, lane
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   for (int c0 = 0; c0 < KC; c0 += 2) {
     const int c = c0 + cs;
     uint32_t lo = 0, hi = 0, sf = 0;
-    if (p < NB && c < KC) {
+    if (row_ok && c < KC && (4 * c + j) * kBlock < Kd) {
       const uint4* src =
           reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + (4 * c + j) * kBlock);
       uint4 u0 = src[0], u1 = src[1];
@@ -140,7 +147,7 @@ hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_
   weight_amax_kernel<<<dim3(parts, E), 256, 0, s>>>(w, per_expert, parts, partials);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int NB = N / kColBlock, KC = Kd / kChunk;
+  const int NB = col_blocks(N, gated_I), KC = padded_k(Kd) / kChunk;
   const int NBp = padded_col_blocks(NB);
   weight_quant_kernel<<<dim3(NBp, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, NBp, KC, partials, parts,
                                                    fold_a, codes, scales, alpha);

@@ -14,6 +14,13 @@
         <copy write dir> <copy bytes> <mfma counter dir> <workload> <out.txt> "<commands>"
         every pmoe kernel: HBM bytes and GB/s, MFMA instructions and busy fraction
 
+    python -m precision_moe_amd.profiling spans <rocprofv3 csv dir> <workload> <out.txt>
+        "<command>" <kernel> <first pair> <pairs>
+        in-step span of a grouped GEMM run as two half launches on two streams:
+        its dispatches by start time, taken two at a time (the two parts of one
+        step), each pair from the first start to the last end; the mean over all
+        pairs and over pairs [first, first + pairs)
+
 The traffic summary records a hash of the GEMM sources it was measured with
 (comments and whitespace excluded); bench.py reports the figure only while the
 sources still match.
@@ -128,6 +135,42 @@ def first_dispatches(directory, kernel, n):
     return [(int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3 for r in rows[:n]]
 
 
+def dispatch_times(directory, kernel):
+    """(start, end) in ns of every dispatch of `kernel` (exact short name), by start time."""
+    rows = [r for r in _rows(directory, "*kernel_trace.csv")
+            if _short(_col(r, "Kernel_Name")) == kernel]
+    t = [(int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp"))) for r in rows]
+    return sorted(t)
+
+
+def pair_spans(times):
+    """Spans (us) of consecutive dispatch pairs: first start to last end of each pair."""
+    return [(max(times[i][1], times[i + 1][1]) - min(times[i][0], times[i + 1][0])) / 1e3
+            for i in range(0, len(times) - 1, 2)]
+
+
+def write_spans(directory, workload, out, command, kernel, first, count):
+    times = dispatch_times(directory, kernel)
+    spans = pair_spans(times)
+    own = [(e - b) / 1e3 for b, e in times]
+    sel = spans[first:first + count]
+    mean = lambda v: sum(v) / max(len(v), 1)
+    lines = [f"# rocprofv3 kernel trace, workload {workload}: in-step span of {kernel}",
+             f"# command: {command}",
+             "# dispatches by start time, two per step (the two parts of the experts on two "
+             "streams); span = first start to last end of a pair",
+             f"kernel={kernel}",
+             f"workload={workload}",
+             f"dispatches={len(times)}",
+             f"avg_dispatch_us={mean(own):.2f}",
+             f"pairs={len(spans)}",
+             f"avg_span_us_all_pairs={mean(spans):.2f}",
+             f"pairs_selected={first}..{first + len(sel) - 1}",
+             f"avg_span_us_selected={mean(sel):.2f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, workload, out, command):
     def one(d, counter):
         vals = {k: v for k, v in counter_means(d, counter).items() if kernel in k}
@@ -225,6 +268,9 @@ if __name__ == "__main__":
     elif cmd == "traffic":
         write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7],
                       sys.argv[8], sys.argv[9], sys.argv[10])
+    elif cmd == "spans":
+        write_spans(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], int(sys.argv[7]),
+                    int(sys.argv[8]))
     elif cmd == "table":
         write_table(*sys.argv[2:7], int(sys.argv[7]), *sys.argv[8:12])
     else:

@@ -27,6 +27,10 @@ Workloads (H hidden, I intermediate, E local experts, K top-k):
   ep4_t1024 T=1024 (same as ep4_t512)
   large     T=4096 H=7168 I=2048 E=256 K=8 swiglu  x~N(0,1), 0.5% of elements x50;
             logits U(0,1), no renormalization
+  nemo_swiglu / nemo_relu2  T=64 H=2688 I=1344 E=8 K=2  x~N(0,1): the Nemotron hidden
+            width with an intermediate width that is a multiple of 64 but not of 128
+  odd_swiglu (T=1100) / odd_relu2 (T=48)  H=2064 I=1040 E=6 K=2  x~N(0,1): widths that
+            are multiples of 16 only
 Weights ~N(0, 0.02) in BF16; router logits ~N(0,1) unless stated; softmax over
 all local experts, top-k by descending probability, lower expert id first.
 """
@@ -86,6 +90,15 @@ WORKLOADS = {
     # the single-GPU shape of [Megatron-LM #8262 . Performance] (all 256 experts
     # local, squared ReLU, top-8), at 512 tokens: a context point, not a test config
     "dsv3_relu2_t512": Workload("dsv3_relu2_t512", 5, 512, 7168, 2048, 256, 8, "relu2"),
+    # the Nemotron hidden width of [Megatron-LM #8262 . Why CuTe DSL] with I = 1344: a
+    # SwiGLU FC1 (N1 = 2688) and the FC2 (N = 2688) end in a column tile that is partly
+    # padding, and I is a multiple of 64 but not of 128
+    "nemo_swiglu": Workload("nemo_swiglu", 6, 64, 2688, 1344, 8, 2, "swiglu"),
+    "nemo_relu2": Workload("nemo_relu2", 7, 64, 2688, 1344, 8, 2, "relu2"),
+    # widths that are multiples of 16 but not of 64 (H) or 32 (I): the library pads
+    # the reductions to whole 64-element chunks and the output columns to whole blocks
+    "odd_swiglu": Workload("odd_swiglu", 8, 1100, 2064, 1040, 6, 2, "swiglu"),
+    "odd_relu2": Workload("odd_relu2", 9, 48, 2064, 1040, 6, 2, "relu2"),
 }
 
 

@@ -55,6 +55,11 @@ def test_version_and_sizes():
     assert pm.weight_bytes(E, I, H, I) == (E * pad(I) * H // 2, E * pad(I) * H // 16, E * pad(H) * I // 2,
                                           E * pad(H) * I // 16)
     assert pm.lib().pmoe_prepare_workspace_bytes(E, I, H, I) > 0
+    # H and I multiples of 16: column blocks of a gated FC1 per half (ceil(I/32) each), and
+    # the reduction padded to whole chunks of 64
+    E, H, I = 2, 80, 48
+    assert pm.weight_bytes(E, 2 * I, H, I) == (E * 256 * 128 // 2, E * 256 * 128 // 16,
+                                              E * 256 * 64 // 2, E * 256 * 64 // 16)
 
 
 def test_workspace_layout_is_aligned_and_large_enough():
@@ -79,7 +84,8 @@ def test_weight_shape_errors(E, N1, H, I):
 
 @pytest.mark.parametrize("T,K,E,H,I,act,code", [
     (-1, 2, 4, 256, 128, 0, 3), (8, 0, 4, 256, 128, 0, 3), (8, 5, 4, 256, 128, 0, 3),
-    (8, 33, 64, 256, 128, 0, 3), (8, 2, 4, 250, 128, 0, 3), (8, 2, 4, 256, 96, 0, 3),
+    (8, 33, 64, 256, 128, 0, 3), (8, 2, 4, 250, 128, 0, 3), (8, 2, 4, 256, 100, 0, 3),
+    (8, 2, 4, 256, 8, 0, 3), (8, 2, 4, 16400, 128, 0, 3),
     (8, 2, 1025, 256, 128, 0, 3), (8, 2, 4, 256, 128, 7, 4)])
 def test_moe_shape_errors(T, K, E, H, I, act, code):
     N1 = 2 * I if act == 1 else I

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import bf16_bits, canonical_from_prepared, dev, dev_bf16
+from helpers import oracle_weights, bf16_bits, canonical_from_prepared, dev, dev_bf16
 from oracle import moe as om
 from oracle import quant as oq
 from oracle.formats import f32_to_bf16_rne
@@ -110,7 +110,7 @@ def test_prepare_weights_small(pm, name):
     w1, w2 = synth.all_weights(w, device="cuda")
     P = pm.prepare_weights(w1, w2)
     _sync()
-    oW = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    oW = oracle_weights(w)
     experts = range(w.E) if w.E <= 4 else [0, 1, w.E // 2, w.E - 1]
     _check_prepared(P, oW, w.E, w.N1, w.H, w.I, experts)
 
@@ -141,7 +141,7 @@ def test_prepare_weights_ep4_sampled_and_refresh(pm):
     _sync()
     ptrs = [t.data_ptr() for t in (P.w1_codes, P.w1_scales, P.w1_alpha, P.w2_codes, P.w2_scales, P.w2_alpha)]
     sample = [0, 47, 95]
-    oW = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    oW = oracle_weights(w)
     _check_prepared(P, oW, w.E, w.N1, w.H, w.I, sample)
     w_new = w.with_(weight_epoch=1)
     n1, n2 = synth.all_weights(w_new, device="cuda")
@@ -149,7 +149,7 @@ def test_prepare_weights_ep4_sampled_and_refresh(pm):
     _sync()
     assert P2 is P and ptrs == [t.data_ptr() for t in (P.w1_codes, P.w1_scales, P.w1_alpha, P.w2_codes,
                                                       P.w2_scales, P.w2_alpha)]
-    oW2 = om.LazyWeights(lambda e: synth.expert_weights(w_new, e), w.E, w.N1, w.H, w.I)
+    oW2 = oracle_weights(w_new)
     _check_prepared(P, oW2, w.E, w.N1, w.H, w.I, [48])
     del w1, w2, n1, n2
     torch.cuda.empty_cache()

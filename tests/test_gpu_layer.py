@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import bf16_bits, dev, dev_bf16
+from helpers import oracle_weights, bf16_bits, dev, dev_bf16
 from oracle import layer as ol
 from oracle import moe as om
 from oracle import quant as oq
@@ -104,7 +104,7 @@ class ExRun:
 
 
 def _oracle(w, x, ids, wts, recipe="per_token", **kw):
-    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    W = oracle_weights(w)
     xin = oq.quantize_input_per_token(x) if recipe == "per_token" else x
     return orc.routed_moe_recipe(recipe, xin, ids, wts, W, w.act, **kw)
 
@@ -357,3 +357,39 @@ def test_forward_repeat_determinism_full_size(pm):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"repeat {i}"
     del P, ws
     torch.cuda.empty_cache()
+
+
+def test_side_stream_with_allocator_churn(pm):
+    """Calls on a stream other than torch's current one: inputs produced on the current stream
+    right before the call are waited for, and the temporaries the binding allocates (workspace,
+    output, contiguous copies) are not handed out again by the caching allocator while the
+    call's kernels still use them, even when the current stream frees and refills memory at
+    once."""
+    import torch
+    w = synth.WORKLOADS["swiglu"]
+    x = dev_bf16(synth.activations(w))
+    ids, wts = synth.router(w)
+    P = pm.prepare_weights(*synth.all_weights(w, device="cuda"))
+    ref = pm.moe_forward(x, dev(ids), dev(wts), P)
+    xq, xs, xg = pm.quantize_input_per_token(x)
+    ref2 = pm.routed_moe(xq, xs, xg, dev(ids), dev(wts), P)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for i in range(6):
+        xi = x.clone()                                           # made on the current stream
+        ids_nc = dev(ids.astype(np.int64).T.copy()).t()          # non-contiguous: copied inside
+        if i % 2 == 0:
+            o = pm.moe_forward(xi, ids_nc, dev(wts), P, stream=side)
+        else:
+            q = pm.quantize_input_per_token(xi, stream=side)
+            o = pm.routed_moe(*q, ids_nc, dev(wts), P, stream=side)
+            del q
+        del xi, ids_nc
+        junk = [torch.full((1 << 18,), -1, dtype=torch.int32, device="cuda") for _ in range(48)]
+        del junk
+        outs.append(o)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        want = ref if i % 2 == 0 else ref2
+        assert torch.equal(o.view(torch.int16), want.view(torch.int16)), i

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import bf16_bits, dev, dev_bf16
+from helpers import (bf16_bits, dev, dev_bf16, oracle_weights, sample_experts, sample_tokens,
+                     split_expert)
 from oracle import moe as om
 from oracle import quant as oq
 from oracle.formats import bf16_to_f32
@@ -73,12 +74,36 @@ class GpuCase:
 
 def _oracle(w, x, ids, wts, tokens=None, experts=None, weights=None):
     xq, xs, xg = oq.quantize_input_per_token(x)
-    W = weights or om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    W = weights or oracle_weights(w)
     return om.routed_moe(xq, xs, xg, ids, wts, W, w.act, tokens=tokens, experts=experts)
 
 
+def _sampled_parity(w, run, n_tokens=8):
+    """z rows of every sampled expert (first, ordinary, both sides of the two-stream split,
+    the hot ones, the last) and the outputs of n_tokens tokens (three of them routed only to
+    experts of the second stream) against the oracle. Returns (experts, tokens)."""
+    v = run.views
+    offs = v["expert_offsets"].cpu().numpy()
+    split = split_expert(offs, v["counters"].cpu().numpy())
+    assert 0 < split < w.E, split
+    experts = sample_experts(np.diff(offs), split)
+    tokens, need = sample_tokens(run.ids, split, experts, n=n_tokens, E=w.E)
+    W = oracle_weights(w, need)
+    res = _oracle(w, run.x, run.ids, run.wts, experts=experts, weights=W)
+    z = bf16_bits(v["z"])
+    for e in experts:
+        rows = np.arange(offs[e], offs[e + 1])
+        rows = rows[res.computed_rows[rows]]
+        assert rows.size > 0, e
+        _assert_rows_close(z[rows], res.z[rows], f"z of expert {e}")
+    res_t = _oracle(w, run.x, run.ids, run.wts, tokens=tokens, weights=W)
+    _assert_rows_close(run.out_bits()[tokens], res_t.out[tokens], f"out of tokens {tokens}")
+    assert any((run.ids[t] >= split).all() for t in tokens)
+    return experts, tokens
+
+
 # ----------------------------------------------------------------------------- small: everything
-@pytest.mark.parametrize("name", ["tiny", "swiglu"])
+@pytest.mark.parametrize("name", ["tiny", "swiglu", "nemo_swiglu", "nemo_relu2"])
 def test_moe_matches_oracle_small(pm, name):
     w = synth.WORKLOADS[name]
     run = GpuCase(pm, w)
@@ -98,17 +123,11 @@ def test_moe_matches_oracle_small(pm, name):
 
 
 def test_moe_relu2_sampled(pm):
-    """relu2 workload (T=1024, H=4096, I=2048, E=64, top-6): rows of two experts and two tokens."""
+    """relu2 workload (T=1024, H=4096, I=2048, E=64, top-6): z rows of experts on both
+    streams and the outputs of 8 tokens."""
     w = synth.WORKLOADS["relu2"]
     run = GpuCase(pm, w)
-    experts = [0, 37]
-    res = _oracle(w, run.x, run.ids, run.wts, experts=experts)
-    rows = np.nonzero(res.computed_rows)[0]
-    assert rows.size > 0
-    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
-    toks = [3, 1000]
-    res_t = _oracle(w, run.x, run.ids, run.wts, tokens=toks)
-    _assert_rows_close(run.out_bits()[toks], res_t.out[toks], "out")
+    _sampled_parity(w, run)
 
 
 def test_fc1_accumulation_within_summation_bound(pm):
@@ -121,7 +140,7 @@ def test_fc1_accumulation_within_summation_bound(pm):
     w = synth.WORKLOADS["relu2"]
     run = GpuCase(pm, w)
     xq, xs, xg = oq.quantize_input_per_token(run.x)
-    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    W = oracle_weights(w)
     rt = om.route(run.ids, w.E)
     h_gpu = run.views["h"].cpu().numpy()
     u = 2.0 ** -23
@@ -145,26 +164,25 @@ def test_fc1_accumulation_within_summation_bound(pm):
 # ----------------------------------------------------------------------------- full size
 @pytest.mark.parametrize("name", ["ep4_t512", "ep4_t1024"])
 def test_moe_ep4_sampled(pm, name):
-    """The EP4 one-GPU share (E=96, H=7168, I=3072, top-6, two hot experts)."""
+    """The EP4 one-GPU share (E=96, H=7168, I=3072, top-6, two hot experts), in the launch
+    configuration the bench times (two streams): z rows of experts on both streams --
+    including both sides of the split and the hot expert of the second stream -- and
+    the outputs of 8 tokens."""
     import torch
     w = synth.WORKLOADS[name]
     run = GpuCase(pm, w)
     counts = np.diff(run.views["expert_offsets"].cpu().numpy())
     assert counts[0] > 5 * np.median(counts)                         # a hot expert spans many M-tiles
-    experts = [0, 17]
-    res = _oracle(w, run.x, run.ids, run.wts, experts=experts)
-    rows = np.nonzero(res.computed_rows)[0]
-    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
-    tok = int(np.nonzero((run.ids == 0).any(axis=1))[0][0])           # one token that uses expert 0
-    res_t = _oracle(w, run.x, run.ids, run.wts, tokens=[tok])
-    _assert_rows_close(run.out_bits()[[tok]], res_t.out[[tok]], "out")
+    experts, _ = _sampled_parity(w, run)
+    assert 48 in experts and w.E - 1 in experts
     del run
     torch.cuda.empty_cache()
 
 
 def test_large_batch_invariance_and_refresh(pm):
-    """T=4096, E=256, H=7168, I=2048, top-8: T=1 vs T=4096 bitwise, then an in-place
-    refresh with new weights tracks the oracle of the new weights."""
+    """T=4096, E=256, H=7168, I=2048, top-8: T=1 vs T=4096 bitwise, sampled z rows and 8
+    tokens against the oracle, then an in-place refresh with new weights tracks the oracle
+    of the new weights."""
     import torch
     w = synth.WORKLOADS["large"]
     run = GpuCase(pm, w)
@@ -172,9 +190,8 @@ def test_large_batch_invariance_and_refresh(pm):
     for t in (0, 2047, 4095):
         one = GpuCase(pm, w, T=1, x=run.x[t:t + 1], ids=run.ids[t:t + 1], wts=run.wts[t:t + 1], weights=run.P)
         assert np.array_equal(one.out_bits()[0], full[t]), f"token {t}"
-    res = _oracle(w, run.x, run.ids, run.wts, experts=[5])
-    rows = np.nonzero(res.computed_rows)[0]
-    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
+    experts, _ = _sampled_parity(w, run)
+    assert max(experts) >= 114
     # in-place refresh
     w2 = w.with_(weight_epoch=1)
     ptr = run.P.w1_codes.data_ptr()
@@ -182,10 +199,49 @@ def test_large_batch_invariance_and_refresh(pm):
     again = GpuCase(pm, w, x=run.x, ids=run.ids, wts=run.wts, weights=run.P)
     assert run.P.w1_codes.data_ptr() == ptr
     assert not np.array_equal(again.out_bits(), full)
-    res2 = _oracle(w2, run.x, run.ids, run.wts, experts=[5])
+    res2 = _oracle(w2, run.x, run.ids, run.wts, experts=[5, 200], weights=oracle_weights(w2, [5, 200]))
     rows = np.nonzero(res2.computed_rows)[0]
     _assert_rows_close(bf16_bits(again.views["z"])[rows], res2.z[rows], "z after refresh")
     del run, again
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["ep4_t1024", "large"])
+def test_plausibility_against_bf16_moe(pm, name):
+    """The GPU output of 8 sampled tokens against the unquantized MoE on the same BF16
+    inputs and weights (float64, the oracle's bf16_reference_moe, one token at a time over
+    that token's experts): per-token cosine mean > 0.97 and min > 0.95, relative error in
+    the band expected of 4-bit weights and activations."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    from helpers import oracle_threads
+    w = synth.WORKLOADS[name]
+    run = GpuCase(pm, w)
+    tokens, need = sample_tokens(run.ids, 0, (), n=8, n_part2=0, E=w.E)
+    bf16_w = {}
+
+    def gen(e):
+        bf16_w[e] = synth.expert_weights(w, e)
+
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        list(ex.map(gen, need))
+
+    def ref_token(t):
+        ex_t = [int(e) for e in run.ids[t]]
+        w1 = np.stack([bf16_w[e][0] for e in ex_t])
+        w2 = np.stack([bf16_w[e][1] for e in ex_t])
+        local = np.arange(len(ex_t), dtype=np.int32)[None]
+        return om.bf16_reference_moe(run.x[t:t + 1], local, run.wts[t:t + 1], w1, w2, w.act)[0]
+
+    with ThreadPoolExecutor(max(1, oracle_threads() // 4)) as ex:
+        ref = np.stack(list(ex.map(ref_token, tokens)))
+    got = bf16_to_f32(run.out_bits()[tokens]).astype(np.float64)
+    cos = np.sum(got * ref, 1) / (np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"{name}: cosine mean {cos.mean():.4f} min {cos.min():.4f}, relative error {rel:.3f}")
+    assert cos.mean() > 0.97 and cos.min() > 0.95, cos
+    assert 0.03 < rel < 0.35, rel
+    del run
     torch.cuda.empty_cache()
 
 
@@ -270,6 +326,17 @@ def test_pointer_and_workspace_errors_leave_output_untouched(pm):
     raw = torch.empty(run.xq.numel() + 16, dtype=torch.uint8, device="cuda")
     expect(2, xq=raw[4:4 + run.xq.numel()].view(run.xq.shape))         # not 16-byte aligned
     expect(2, x_scale=None)                                            # null
+    wsb = torch.empty(run.ws.numel() + 256, dtype=torch.uint8, device="cuda")
+    expect(2, ws=wsb[16:16 + run.ws.numel()])                          # ws 16- but not 256-byte aligned
+    raw64 = torch.zeros(ids.numel() * 2 + 2, dtype=torch.int32, device="cuda")
+    ids64 = raw64[1:1 + ids.numel() * 2]                               # int64 ids 4- but not 8-byte aligned
+    rc = pm.lib().pmoe_routed_moe(pm._ptr(run.xq), pm._ptr(run.xs), pm._ptr(run.xg), pm._ptr(ids64),
+                                  pm.IDS_INT64, pm._ptr(wts), w.T, w.K, w.E, w.H, w.I, run.P.N1, 0,
+                                  pm._ptr(run.P.w1_codes), pm._ptr(run.P.w1_scales),
+                                  pm._ptr(run.P.w1_alpha), pm._ptr(run.P.w2_codes),
+                                  pm._ptr(run.P.w2_scales), pm._ptr(run.P.w2_alpha), run.P.act,
+                                  pm._ptr(run.ws), run.ws.numel(), pm._ptr(out), pm._stream())
+    assert rc == 2 and "8-byte" in pm.lib().pmoe_last_error().decode()
     need = pm.moe_workspace_bytes(w.T, w.K, w.E, w.H, w.I, run.P.act)
     expect(5, ws=torch.empty(need - 1, dtype=torch.uint8, device="cuda"))
     _sync()

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import bf16_bits, dev, dev_bf16
+from helpers import (bf16_bits, dev, dev_bf16, oracle_weights, oracle_weights_per_tensor,
+                     sample_experts, sample_tokens, split_expert)
 from oracle import moe as om
 from oracle import quant as oq
 from oracle import recipes as orc
@@ -59,7 +60,7 @@ def _a1(x_bits):
 def _a2_from_oracle(w, x, ids, wts, experts=None):
     """Calibrate the FC2 input scale on the oracle's per-token intermediate."""
     xq, xs, xg = oq.quantize_input_per_token(x)
-    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+    W = oracle_weights(w, experts if experts is not None else ())
     res = om.routed_moe(xq, xs, xg, ids, wts, W, w.act, experts=experts)
     return F32(F32(2688.0) / F32(np.abs(res.h[res.computed_rows]).max()))
 
@@ -111,8 +112,8 @@ class PerTensorRun:
         self.views = pm.workspace_views(self.ws, self.T, K, w.E, w.H, w.I, self.P.act)
 
 
-def _oracle_per_tensor(w, x, ids, wts, a1, a2, **kw):
-    W = orc.LazyWeightsPerTensor(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I, a1, a2)
+def _oracle_per_tensor(w, x, ids, wts, a1, a2, need=(), **kw):
+    W = oracle_weights_per_tensor(w, a1, a2, need)
     return orc.routed_moe_recipe("per_tensor", orc.quantize_input_per_tensor(x, a1), ids, wts, W,
                                  w.act, a2=a2, **kw)
 
@@ -134,21 +135,39 @@ def test_per_tensor_moe_small(pm, name):
     _assert_rows_close(bf16_bits(run.out), res.out, "out")
 
 
+def _sample(w, views, ids):
+    """Experts on both streams (split sides, hot, first, last) and 8 tokens, three of them
+    routed only to experts of the second stream; plus every expert those need."""
+    offs = views["expert_offsets"].cpu().numpy()
+    split = split_expert(offs, views["counters"].cpu().numpy())
+    experts = sample_experts(np.diff(offs), split)
+    tokens, need = sample_tokens(ids, split, experts, n=8, E=w.E)
+    return experts, tokens, need
+
+
+def _check_sampled(w, run_z, run_out, views, res, res_t, experts, tokens):
+    offs = views["expert_offsets"].cpu().numpy()
+    z = bf16_bits(run_z)
+    for e in experts:
+        rows = np.arange(offs[e], offs[e + 1])
+        rows = rows[res.computed_rows[rows]]
+        assert rows.size > 0, e
+        _assert_rows_close(z[rows], res.z[rows], f"z of expert {e}")
+    _assert_rows_close(bf16_bits(run_out)[tokens], res_t.out[tokens], f"out of tokens {tokens}")
+
+
 @pytest.mark.parametrize("name", ["relu2", "ep4_t1024", "large"])
 def test_per_tensor_moe_sampled(pm, name):
     import torch
     w = synth.WORKLOADS[name]
     x = synth.activations(w)
     ids, wts = synth.router(w)
-    experts = [0, 17]
-    a1, a2 = _a1(x), _a2_from_oracle(w, x, ids, wts, experts=experts)
+    a1, a2 = _a1(x), _a2_from_oracle(w, x, ids, wts, experts=[0, 17])
     run = PerTensorRun(pm, w, a1, a2)
-    res = _oracle_per_tensor(w, x, ids, wts, a1, a2, experts=experts)
-    rows = np.nonzero(res.computed_rows)[0]
-    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
-    tok = int(np.nonzero((ids == 0).any(axis=1))[0][0])
-    res_t = _oracle_per_tensor(w, x, ids, wts, a1, a2, tokens=[tok])
-    _assert_rows_close(bf16_bits(run.out)[[tok]], res_t.out[[tok]], "out")
+    experts, tokens, need = _sample(w, run.views, ids)
+    res = _oracle_per_tensor(w, x, ids, wts, a1, a2, need=need, experts=experts)
+    res_t = _oracle_per_tensor(w, x, ids, wts, a1, a2, tokens=tokens)
+    _check_sampled(w, run.views["z"], run.out, run.views, res, res_t, experts, tokens)
     del run
     torch.cuda.empty_cache()
 
@@ -171,8 +190,8 @@ class W4A16Run:
         self.views = pm.workspace_views(self.ws, self.T, K, w.E, w.H, w.I, self.P.act)
 
 
-def _oracle_w4a16(w, x, ids, wts, **kw):
-    W = om.LazyWeights(lambda e: synth.expert_weights(w, e), w.E, w.N1, w.H, w.I)
+def _oracle_w4a16(w, x, ids, wts, need=(), **kw):
+    W = oracle_weights(w, need)
     return orc.routed_moe_recipe("weight_only", x, ids, wts, W, w.act, **kw)
 
 
@@ -197,13 +216,10 @@ def test_w4a16_moe_sampled(pm, name):
     import torch
     w = synth.WORKLOADS[name]
     run = W4A16Run(pm, w)
-    experts = [0, 17]
-    res = _oracle_w4a16(w, run.x, run.ids, run.wts, experts=experts)
-    rows = np.nonzero(res.computed_rows)[0]
-    _assert_rows_close(bf16_bits(run.views["z"])[rows], res.z[rows], "z")
-    tok = int(np.nonzero((run.ids == 0).any(axis=1))[0][0])
-    res_t = _oracle_w4a16(w, run.x, run.ids, run.wts, tokens=[tok, 5])
-    _assert_rows_close(bf16_bits(run.out)[[tok, 5]], res_t.out[[tok, 5]], "out")
+    experts, tokens, need = _sample(w, run.views, run.ids)
+    res = _oracle_w4a16(w, run.x, run.ids, run.wts, need=need, experts=experts)
+    res_t = _oracle_w4a16(w, run.x, run.ids, run.wts, tokens=tokens)
+    _check_sampled(w, run.views["z"], run.out, run.views, res, res_t, experts, tokens)
     del run
     torch.cuda.empty_cache()
 
