@@ -270,6 +270,27 @@ int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x_scale,
                     const void* w2_codes, const void* w2_scales, const float* w2_alpha,
                     int act, void* ws, size_t ws_bytes, void* out, void* stream);
 
+/*
+ * pmoe_routed_moe for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments without ws / ws_bytes, the same results bit for bit. The
+ * workspace is a static device array of PMOE_STATIC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends; the call
+ * allocates nothing (no hipMalloc, no library stream or event: everything runs
+ * on `stream`). Sizes whose workspace (pmoe_moe_workspace_bytes) exceeds the
+ * scratch are PMOE_ERR_WORKSPACE -- at H = 7168, I = 3072 that is about 2300
+ * routes (T*K). Every call on one device shares that device's scratch: calls
+ * that overlap in time on one device (two streams, two host threads) race and
+ * corrupt each other's results; serialize them.
+ */
+#define PMOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int pmoe_routed_moe_static(const void* xq, const void* x_sf, const float* x_scale,
+                           const void* topk_ids, int ids_type, const float* topk_w,
+                           int T, int K, int E, int H, int I, int N1, int expert_offset,
+                           const void* w1_codes, const void* w1_scales, const float* w1_alpha,
+                           const void* w2_codes, const void* w2_scales, const float* w2_alpha,
+                           int act, void* out, void* stream);
+
 /* Steps of pmoe_routed_moe, for callers that time or interleave them. */
 #define PMOE_STEP_ROUTE 0    /* histogram, scan, tile list, scatter (3 kernels)   */
 #define PMOE_STEP_FC1 1      /* FC1 grouped GEMM + activation -> h                */

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "pmoe_moe_workspace_layout": (_i, [_i, _i, _i, _i, _i, _i, _c_size_p]),
     "pmoe_routed_moe": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
                              _vp, _vp, _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
+    "pmoe_routed_moe_static": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _i, _vp, _vp]),
     "pmoe_routed_moe_steps": (_i, [_i, _i, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, ctypes.c_size_t, _vp, _vp]),
     "pmoe_finalize": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
@@ -344,6 +346,30 @@ def routed_moe(xq, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, ac
         _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, _ptr(workspace),
         workspace.numel(), _ptr(out),
         _stream(stream, xq, x_sf, x_scale, topk_ids, topk_w, workspace, out, W.w1_codes, W.w1_scales, W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def routed_moe_static(xq, x_sf, x_scale, topk_ids, topk_w, weights: PreparedWeights, act=None,
+                      expert_offset=0, out=None, stream=None):
+    """routed_moe on the library's static scratch (pmoe_routed_moe_static): no workspace
+    argument and no device allocation inside the call; `out` should be given by callers
+    that cannot allocate (else one BF16 [T, H] tensor is allocated here)."""
+    import torch
+    T, K = topk_ids.shape
+    W = weights
+    act = W.act if act is None else act
+    topk_ids, ids_type, topk_w = _routing_args(topk_ids, topk_w)
+    if out is None:
+        out = torch.empty((T, W.H), dtype=torch.bfloat16, device=xq.device)
+    _check(lib().pmoe_routed_moe_static(
+        _ptr(xq), _ptr(x_sf), _ptr(x_scale), _ptr(topk_ids), ids_type, _ptr(topk_w), T, K, W.E, W.H,
+        W.I, W.N1, expert_offset, _ptr(W.w1_codes), _ptr(W.w1_scales), _ptr(W.w1_alpha),
+        _ptr(W.w2_codes), _ptr(W.w2_scales), _ptr(W.w2_alpha), act, _ptr(out),
+        _stream(stream, xq, x_sf, x_scale, topk_ids, topk_w, out, W.w1_codes, W.w1_scales,
+                W.w1_alpha, W.w2_codes, W.w2_scales, W.w2_alpha)))
     return out
 
 

@@ -392,6 +392,37 @@ int aux_for_current_device(Aux** out) {
   return PMOE_OK;
 }
 
+// ------------------------------------------------------------------ static scratch
+// The workspace of pmoe_routed_moe_static, for callers that cannot allocate
+// device memory: one file-scope device array, which every device the library
+// runs on holds (its own copy, at its own address) until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, looked up once per device
+// on the entry point's first call there (with that device current) and kept.
+constexpr size_t kScratchBytes = PMOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // device address of `scratch` per device, null until looked up
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(PMOE_ERR_DEVICE, "no usable current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(PMOE_ERR_HIP, std::string("looking up the static scratch: ") + hipGetErrorString(e));
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return PMOE_OK;
+}
+
 // Steps first..last of the routed path under one recipe.
 //   per-token : x = xq, x_sf, x_scale (per-token NVFP4); requant per row.
 //   per-tensor: x = xq, x_sf (static scale folded into the alphas); x_scale
@@ -406,7 +437,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
              const void* w2_scales, const float* w2_alpha, int act, void* ws, size_t ws_bytes,
              void* out, void* stream, bool fused = false, float swiglu_limit = 0.0f,
              int streams = 0, bool bf16_input = false, const float* a1 = nullptr,
-             void* const* step_events = nullptr) {
+             void* const* step_events = nullptr, bool static_ws = false) {
   if (first < PMOE_STEP_ROUTE || last > PMOE_STEP_FINALIZE || first > last)
     return fail(PMOE_ERR_ARG, "need 0 <= first <= last <= 4");
   if (!(swiglu_limit >= 0.0f)) return fail(PMOE_ERR_ARG, "swiglu_limit must be >= 0");
@@ -441,7 +472,7 @@ int moe_path(Recipe rc, int first, int last, const void* x, const void* x_sf, co
   PMOE_TRY(check_ptr(w2_codes, 16, "w2_codes"));
   PMOE_TRY(check_ptr(w2_scales, 16, "w2_scales"));
   PMOE_TRY(check_ptr(w2_alpha, 4, "w2_alpha"));
-  PMOE_TRY(check_ptr(ws, 256, "ws"));
+  if (!static_ws) PMOE_TRY(check_ptr(ws, 256, "ws"));  // the static scratch is known good
   PMOE_TRY(check_ptr(out, 16, "out"));
   const MoeLayout L = moe_layout(T, K, E, H, I);
   if (ws_bytes < L.total)
@@ -678,6 +709,31 @@ PMOE_EXPORT int pmoe_routed_moe(const void* xq, const void* x_sf, const float* x
   return moe_path(kPerToken, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, x_scale, nullptr,
                   topk_ids, ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales,
                   w1_alpha, w2_codes, w2_scales, w2_alpha, act, ws, ws_bytes, out, stream);
+}
+
+PMOE_EXPORT int pmoe_routed_moe_static(const void* xq, const void* x_sf, const float* x_scale,
+                                       const void* topk_ids, int ids_type, const float* topk_w,
+                                       int T, int K, int E, int H, int I, int N1,
+                                       int expert_offset, const void* w1_codes,
+                                       const void* w1_scales, const float* w1_alpha,
+                                       const void* w2_codes, const void* w2_scales,
+                                       const float* w2_alpha, int act, void* out, void* stream) {
+  PMOE_TRY(check_moe_shape(T, K, E, H, I, act));
+  const size_t need = moe_layout(T, K, E, H, I).total;
+  if (need > kScratchBytes)
+    return fail(PMOE_ERR_WORKSPACE, "pmoe_routed_moe_static: these sizes need " + std::to_string(need) +
+                                        " bytes of scratch; the static scratch holds " +
+                                        std::to_string(kScratchBytes) +
+                                        " (PMOE_STATIC_SCRATCH_BYTES): use pmoe_routed_moe with a workspace");
+  if (T == 0) return ok();
+  PMOE_TRY(check_device());
+  void* ws = nullptr;
+  PMOE_TRY(scratch_for_current_device(&ws));
+  // one stream: no library stream or event is created or used
+  return moe_path(kPerToken, PMOE_STEP_ROUTE, PMOE_STEP_FINALIZE, xq, x_sf, x_scale, nullptr, topk_ids,
+                  ids_type, topk_w, T, K, E, H, I, N1, expert_offset, w1_codes, w1_scales, w1_alpha,
+                  w2_codes, w2_scales, w2_alpha, act, ws, kScratchBytes, out, stream, false, 0.0f, 1,
+                  false, nullptr, nullptr, true);
 }
 
 PMOE_EXPORT int pmoe_routed_moe_per_tensor(const void* xq, const void* x_sf, const void* topk_ids,
