@@ -184,6 +184,17 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, _Float16 sc) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// ------------------------------------------------------------------ barriers
+// Workgroup barrier for hand-offs through LDS only: the fences order this
+// wave's LDS accesses around the barrier (it waits for its own LDS operations,
+// not for global loads still in flight), so prefetches issued before the
+// barrier keep flying. __syncthreads() would also drain every global load.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -78,6 +78,7 @@ struct FcConfig {
 __host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx4 mfma16(half8_t a, half8_t b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -113,12 +114,129 @@ struct BFrag {
   }
 };
 
+// Epilogue of one tile: acc[rb][cb][i] of this wave -> the output. wbuf: this
+// wave's kWaveStage bytes of LDS that no other wave uses any more (the caller
+// has passed the barrier that ends the main loop's reads).
+template <int MODE, int NRB, int AK, int kWaveStage>
+__device__ __forceinline__ void fc_epilogue(const FcParams& P, const floatx4 (&acc)[NRB][4],
+                                            const float* s_row, int row0, int mrows, int p0, int lane,
+                                            uint8_t* wbuf) {
+  // acc[rb][cb][i] is row 16*rb + 4*(lane/16) + i, column 16*cb + lane%16 of
+  // the wave's 64 columns: position p0 + cb/2, half h = cb%2. Only output
+  // columns below P.n_out are written (padding positions and the zero rows
+  // that pad a partial column block are dropped; P.n_out is a multiple of 16).
+  const int n16 = lane & 15;
+  if constexpr (MODE == kFc2Fused) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * rb + 4 * (lane >> 4) + i;
+        if (m >= mrows) continue;
+        const float s = s_row[m];
+        // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
+        const int f = P.out_route[row0 + m];
+        const float wgt = P.out_w[f];
+        float* acc_row = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
+          if (col0 < P.n_out) unsafeAtomicAdd(acc_row + col0, wgt * (acc[rb][h][i] * s));
+          if (col1 < P.n_out) unsafeAtomicAdd(acc_row + col1, wgt * (acc[rb][2 + h][i] * s));
+        }
+      }
+    }
+  } else {
+    // Staged stores: each wave writes its part of the output tile into its own
+    // kWaveStage bytes of free LDS, pass by pass, then copies it out in 16-byte
+    // row-contiguous pieces. The wave's output columns are contiguous: 64
+    // (squared ReLU, FC2) or 32 (SwiGLU: gate and up fold into one). FC1
+    // writes FP32 h for the NVFP4 recipes (requantized next) and BF16 h for
+    // W4A16 (FC2's input as it is); FC2 writes BF16 z.
+    constexpr bool kSwiglu = MODE == kFc1Swiglu;
+    constexpr int kS = (MODE == kFc2 || AK == 1) ? 2 : 4;           // bytes per element
+    constexpr int kCw = kSwiglu ? 32 : 64;                          // columns per wave
+    constexpr int kRowB = kCw * kS;                                 // LDS bytes per row
+    constexpr int kPassRows = (kWaveStage / kRowB) < kTileM ? kWaveStage / kRowB : kTileM;
+    const int col_base = kSwiglu ? kColBlock * (p0 >> 1) : kColBlock * p0;
+    // bytes of an LDS row that exist in the output (whole 16-byte pieces)
+    const int row_bytes = min(max(P.n_out - col_base, 0), kCw) * kS;
+    auto put = [&](int m, int lc, float v) {
+      if constexpr (kS == 2)
+        *reinterpret_cast<uint16_t*>(wbuf + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(v);
+      else
+        *reinterpret_cast<float*>(wbuf + m * kRowB + lc * 4) = v;
+    };
+#pragma unroll
+    for (int r_lo = 0; r_lo < 16 * NRB; r_lo += kPassRows) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (16 * rb + 16 <= r_lo || 16 * rb >= r_lo + kPassRows) continue;  // resolved at compile time
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * rb + 4 * (lane >> 4) + i;
+          if (m >= mrows) continue;
+          const float s = s_row[m];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float c0 = acc[rb][h][i], c1 = acc[rb][2 + h][i];  // positions p0, p0 + 1
+            const int lc = 16 * h + n16;
+            if constexpr (MODE == kFc1Relu2) {
+              const float y0 = __builtin_fmaxf(c0 * s, 0.0f);
+              const float y1 = __builtin_fmaxf(c1 * s, 0.0f);
+              put(m - r_lo, lc, y0 * y0);
+              put(m - r_lo, lc + kColBlock, y1 * y1);
+            } else if constexpr (kSwiglu) {
+              // p0 is even: position p0 holds gate rows, p0 + 1 the matching up rows.
+              float g = c0 * s;
+              float u = c1 * s;
+              if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
+                g = __builtin_fminf(g, P.swiglu_limit);
+                u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
+              }
+              // hardware exp and reciprocal (a few ulp; h is compared to
+              // tolerance, and the requant works on whatever h this writes)
+              const float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              put(m - r_lo, lc, silu * u);
+            } else {
+              put(m - r_lo, lc, c0 * s);
+              put(m - r_lo, lc + kColBlock, c1 * s);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int nrow = min(kPassRows, mrows - r_lo);
+      uint8_t* out = static_cast<uint8_t*>(P.out) + ((long)(row0 + r_lo) * P.out_stride + (long)col_base) * kS;
+#pragma unroll
+      for (int k = 0; k < kPassRows * kRowB / (64 * 16); ++k) {
+        const int off = (k * 64 + lane) * 16;
+        const int r = off / kRowB, cb = off % kRowB;
+        if (r < nrow && cb < row_bytes) {
+          // FC1's h is written once and read once, by the next kernel:
+          // non-temporal stores keep it from displacing the weight slabs
+          // that the M-tiles of an expert share in L2
+          u32x4* dst = reinterpret_cast<u32x4*>(out + (long)r * P.out_stride * kS + cb);
+          const u32x4 val = *reinterpret_cast<const u32x4*>(wbuf + off);
+          if constexpr (MODE == kFc1Swiglu || MODE == kFc1Relu2)
+            __builtin_nontemporal_store(val, dst);
+          else
+            *dst = val;
+        }
+      }
+      if (r_lo + kPassRows < 16 * NRB) __syncthreads();  // the next pass overwrites the buffer
+    }
+  }
+}
+
 // Main loop + epilogue for one tile. NRB: the tile's rows rounded up to 16-row
 // blocks (1..4); blocks past it are neither staged nor multiplied. kNT = 1:
-// the weight loads carry the non-temporal hint (slabs read by this tile only). Every global
-// load inside the loop is unconditional (addresses past the end are out of the
-// buffer range and return zeros, and that data is never used), which keeps the
-// in-order load counters exact so the B ring really stays in flight.
+// the weight loads carry the non-temporal hint (slabs read by this tile only).
+// Every global load inside the loop is unconditional, which keeps the in-order
+// load counters exact so the B ring really stays in flight: prefetches past
+// the last chunk (or stage) re-read the last one -- the chunk index is clamped
+// on the scalar side, because the buffer range check does not cover the
+// scalar offset -- and their data is never used.
 template <int MODE, int NRB, int AK, int kRing, int kNT>
 __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
                                         const int* a_row, const float* s_row, int e, int row0,
@@ -134,7 +252,6 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   // AK = 0: NVFP4 rows (K/2 bytes of codes + K/16 scales per row), decoded
   // exactly to FP16 on the way into LDS. AK = 1: BF16 rows (2K bytes), copied
   // into LDS as they are (W4A16).
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int kAQ = AK == 1 ? 4 : 1;             // 16-byte loads per thread and stage
   const int a_row_bytes = AK == 1 ? KC * 128 : KC * 32;
   const int ar = tid >> 2, aq = tid & 3;
@@ -152,15 +269,19 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     u32x4 q[kAQ];
     uint32_t s;
   };
+  // The stage offset goes into the per-lane offset, which the buffer range
+  // check covers: the half stage that ends an odd chunk count reads past the
+  // end of the row (data never used), and past the last row of the buffer
+  // such reads return zeros instead of touching memory beyond it.
   auto a_copy_load = [&](int st, ARaw& v) {
     if (a_fill) {
       if constexpr (AK == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v.q[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + 16 * i, st * 256, 0);
+          v.q[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + st * 256 + 16 * i, 0, 0);
       } else {
-        v.q[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff, st * 64, 0);
-        v.s = __builtin_amdgcn_raw_buffer_load_b16(a_srsrc, a_svoff, st * 8, 0);
+        v.q[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff + st * 64, 0, 0);
+        v.s = __builtin_amdgcn_raw_buffer_load_b16(a_srsrc, a_svoff + st * 8, 0, 0);
       }
     }
   };
@@ -236,23 +357,24 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   uint32_t rs0[kRing], rs1[kRing];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
-    rq0[i] = load_q(bq_voff0, i);
-    rq1[i] = load_q(bq_voff1, i);
-    rs0[i] = load_s(bs_voff0, i);
-    rs1[i] = load_s(bs_voff1, i);
+    const int ci = min(i, KC - 1);
+    rq0[i] = load_q(bq_voff0, ci);
+    rq1[i] = load_q(bq_voff1, ci);
+    rs0[i] = load_s(bs_voff0, ci);
+    rs1[i] = load_s(bs_voff1, ci);
   }
   {
     ARaw v;
     a_copy_load(0, v);
     a_copy_store(&a_lds[0][0], v);
   }
-  __syncthreads();
+  lds_barrier();
 
   auto chunk = [&](const int c, const uint8_t* abuf, const int half, const int i) {
     // Refill the slot freed by chunk c - 1 before decoding slot i; the
     // scheduling barrier keeps these loads ahead of the decode.
     const int r = (i + kPrefetch) % kRing;
-    const int cn = c + kPrefetch;
+    const int cn = min(c + kPrefetch, KC - 1);
     rq0[r] = load_q(bq_voff0, cn);
     rq1[r] = load_q(bq_voff1, cn);
     rs0[r] = load_s(bs_voff0, cn);
@@ -290,15 +412,16 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
 
   // Full stage st (two chunks) in LDS buffer t, ring slots slot and slot + 1;
   // loads the next stage's A and stores it into the next buffer.
+  const int last_stage = (KC - 1) >> 1;  // stage of the last chunk
   auto stage = [&](const int st, const int t, const int slot) {
     ARaw v;
-    a_copy_load(st + 1, v);  // past the end on the last stage; that copy is unused
+    a_copy_load(min(st + 1, last_stage), v);  // on the last stage a copy that is unused
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* abuf = &a_lds[t][0];
     chunk(2 * st, abuf, 0, slot);
     chunk(2 * st + 1, abuf, 1, slot + 1);
     a_copy_store(&a_lds[(t + 1) % kStages][0], v);
-    __syncthreads();
+    lds_barrier();
   };
 
   // The loop body covers two stages (four chunks): stage j of a pair uses LDS
@@ -325,113 +448,7 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   // The barrier ends every wave's reads of the A stages, which the staged
   // stores below reuse.
   __syncthreads();
-  // acc[rb][cb][i] is row 16*rb + 4*(lane/16) + i, column 16*cb + lane%16 of
-  // the wave's 64 columns: position p0 + cb/2, half h = cb%2. Only output
-  // columns below P.n_out are written (padding positions and the zero rows
-  // that pad a partial column block are dropped; P.n_out is a multiple of 16).
-  const int n16 = lane & 15;
-  if constexpr (MODE == kFc2Fused) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * rb + 4 * (lane >> 4) + i;
-        if (m >= mrows) continue;
-        const float s = s_row[m];
-        // fused finalize: fp32(w * z) added into the token's FP32 row, in any order
-        const int f = P.out_route[row0 + m];
-        const float wgt = P.out_w[f];
-        float* acc_row = static_cast<float*>(P.out) + (long)(f / P.topk) * P.out_stride;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col0 = kColBlock * p0 + 16 * h + n16, col1 = col0 + kColBlock;
-          if (col0 < P.n_out) unsafeAtomicAdd(acc_row + col0, wgt * (acc[rb][h][i] * s));
-          if (col1 < P.n_out) unsafeAtomicAdd(acc_row + col1, wgt * (acc[rb][2 + h][i] * s));
-        }
-      }
-    }
-  } else {
-    // Staged stores: each wave writes its part of the output tile into its own
-    // 8 KB of the (now free) A stage memory, then copies it out in 16-byte
-    // row-contiguous pieces. The wave's output columns are contiguous: 64
-    // (squared ReLU, FC2) or 32 (SwiGLU: gate and up fold into one). FC1
-    // writes FP32 h for the NVFP4 recipes (requantized next) and BF16 h for
-    // W4A16 (FC2's input as it is); FC2 writes BF16 z.
-    constexpr bool kSwiglu = MODE == kFc1Swiglu;
-    constexpr int kS = (MODE == kFc2 || AK == 1) ? 2 : 4;           // bytes per element
-    constexpr int kCw = kSwiglu ? 32 : 64;                          // columns per wave
-    constexpr int kRowB = kCw * kS;                                 // LDS bytes per row
-    constexpr int kPassRows = (8192 / kRowB) < kTileM ? 8192 / kRowB : kTileM;
-    uint8_t* wbuf = &a_lds[0][0] + wave * 8192;
-    const int col_base = kSwiglu ? kColBlock * (p0 >> 1) : kColBlock * p0;
-    // bytes of an LDS row that exist in the output (whole 16-byte pieces)
-    const int row_bytes = min(max(P.n_out - col_base, 0), kCw) * kS;
-    auto put = [&](int m, int lc, float v) {
-      if constexpr (kS == 2)
-        *reinterpret_cast<uint16_t*>(wbuf + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(v);
-      else
-        *reinterpret_cast<float*>(wbuf + m * kRowB + lc * 4) = v;
-    };
-#pragma unroll
-    for (int r_lo = 0; r_lo < 16 * NRB; r_lo += kPassRows) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        if (16 * rb + 16 <= r_lo || 16 * rb >= r_lo + kPassRows) continue;  // resolved at compile time
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * rb + 4 * (lane >> 4) + i;
-          if (m >= mrows) continue;
-          const float s = s_row[m];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float c0 = acc[rb][h][i], c1 = acc[rb][2 + h][i];  // positions p0, p0 + 1
-            const int lc = 16 * h + n16;
-            if constexpr (MODE == kFc1Relu2) {
-              const float y0 = __builtin_fmaxf(c0 * s, 0.0f);
-              const float y1 = __builtin_fmaxf(c1 * s, 0.0f);
-              put(m - r_lo, lc, y0 * y0);
-              put(m - r_lo, lc + kColBlock, y1 * y1);
-            } else if constexpr (kSwiglu) {
-              // p0 is even: position p0 holds gate rows, p0 + 1 the matching up rows.
-              float g = c0 * s;
-              float u = c1 * s;
-              if (P.swiglu_limit > 0.0f) {  // clamp: gate from above, up on both sides
-                g = __builtin_fminf(g, P.swiglu_limit);
-                u = __builtin_fminf(__builtin_fmaxf(u, -P.swiglu_limit), P.swiglu_limit);
-              }
-              // hardware exp and reciprocal (a few ulp; h is compared to
-              // tolerance, and the requant works on whatever h this writes)
-              const float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-              put(m - r_lo, lc, silu * u);
-            } else {
-              put(m - r_lo, lc, c0 * s);
-              put(m - r_lo, lc + kColBlock, c1 * s);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      const int nrow = min(kPassRows, mrows - r_lo);
-      uint8_t* out = static_cast<uint8_t*>(P.out) + ((long)(row0 + r_lo) * P.out_stride + (long)col_base) * kS;
-#pragma unroll
-      for (int k = 0; k < kPassRows * kRowB / (64 * 16); ++k) {
-        const int off = (k * 64 + lane) * 16;
-        const int r = off / kRowB, cb = off % kRowB;
-        if (r < nrow && cb < row_bytes) {
-          // FC1's h is written once and read once, by the next kernel:
-          // non-temporal stores keep it from displacing the weight slabs
-          // that the M-tiles of an expert share in L2
-          u32x4* dst = reinterpret_cast<u32x4*>(out + (long)r * P.out_stride * kS + cb);
-          const u32x4 val = *reinterpret_cast<const u32x4*>(wbuf + off);
-          if constexpr (MODE == kFc1Swiglu || MODE == kFc1Relu2)
-            __builtin_nontemporal_store(val, dst);
-          else
-            *dst = val;
-        }
-      }
-      if (r_lo + kPassRows < 16 * NRB) __syncthreads();  // the next pass overwrites the buffer
-    }
-  }
+  fc_epilogue<MODE, NRB, AK, 8192>(P, acc, s_row, row0, mrows, p0, lane, &a_lds[0][0] + wave * 8192);
 }
 
 template <int MODE, int NRB, int AK, int kRing>
@@ -444,9 +461,13 @@ __device__ __forceinline__ void tile_nt(bool single, const FcParams& P, uint8_t 
     fc_tile<MODE, NRB, AK, kRing, 0>(P, a_lds, a_row, s_row, e, row0, mrows, nt);
 }
 
-template <int MODE, int AK, int kRing>
-__device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
-                                         int* a_row, float* s_row) {
+// The work item of this workgroup -> its expert, rows and column tile; fills
+// the tile's A row indices and row scales in LDS. False: no item (the grid is
+// rounded up), the workgroup returns.
+struct FcItem {
+  int e, row0, mrows, nt, count;
+};
+__device__ __forceinline__ bool fc_item(const FcParams& P, int* a_row, float* s_row, FcItem& it) {
   const int tid = threadIdx.x;
   // Work item -> (tile, column tile): items are numbered expert-major, then
   // column tile, then M-tile; XCD x = blockIdx % 8 takes items
@@ -458,9 +479,9 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
   const int total = (t_hi - t_lo) * NT;
   const int per = (total + 7) >> 3;
   const int j = blockIdx.x >> 3;
-  if (j >= per) return;
+  if (j >= per) return false;
   const int item = t_lo * NT + (blockIdx.x & 7) * per + j;
-  if (item >= t_hi * NT) return;
+  if (item >= t_hi * NT) return false;
   // Every tile entry of an expert holds {expert, its first row, its first
   // tile, its row count}: one load gives the item's rows.
   const int4 ta = reinterpret_cast<const int4*>(P.tiles)[item / NT];
@@ -480,6 +501,16 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
     s_row[tid] = P.a_scale ? P.a_scale[ar] * P.w_alpha[e] : P.w_alpha[e];
   }
   __syncthreads();
+  it = FcItem{e, row0, mrows, nt, count};
+  return true;
+}
+
+template <int MODE, int AK, int kRing>
+__device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLdsStage],
+                                         int* a_row, float* s_row) {
+  FcItem it;
+  if (!fc_item(P, a_row, s_row, it)) return;
+  const int e = it.e, row0 = it.row0, mrows = it.mrows, nt = it.nt, count = it.count;
   switch ((mrows + 15) >> 4) {  // 16-row blocks that hold rows of this tile
     // An expert with one M-tile reads its weight slabs once: its B loads are
     // non-temporal (kNT), so they do not displace the slabs that the M-tiles
