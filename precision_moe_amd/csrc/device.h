@@ -47,22 +47,23 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 // Non-negative finite value (or +inf) -> E4M3fn byte: round to nearest even,
 // saturating at 448 (0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode_sat(float v) {
-  if (!(v < 448.0f)) return 0x7Eu;
-  if (v < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (v*512 is exact)
-    return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8; 8 is 2^-6 = byte 0x08
-  }
-  // Normal: round the 23-bit mantissa to 3 bits (ties to even); a carry moves
-  // into the exponent field, which is what rounding up to the next binade means.
-  uint32_t u = __float_as_uint(v);
-  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-  return (r >> 20) - (120u << 3);  // rebias 127 -> 7
+  // Both forms are computed and one is selected (no branch):
+  // below 2^-6: subnormal grid of step 2^-9 (v*512 is exact), 0..8, where 8
+  // is 2^-6 = byte 0x08;
+  const uint32_t sub = (uint32_t)__builtin_rintf(__builtin_fminf(v, 0.015625f) * 512.0f);
+  // normal: round the 23-bit mantissa to 3 bits (ties to even); a carry moves
+  // into the exponent field, which is what rounding up to the next binade
+  // means; then rebias 127 -> 7.
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  return !(v < 448.0f) ? 0x7Eu : (v < 0.015625f ? sub : nrm);
 }
 
 // E4M3fn byte (sign ignored; never 0x7F here) -> exact float.
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
-  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)(b & 7u) * 0.001953125f;                 // m * 2^-9
+  const float nrm = __uint_as_float(((b & 0x7Fu) << 20) + (120u << 23));  // exponent e + 120, mantissa m
+  return ((b >> 3) & 0xFu) == 0 ? sub : nrm;
 }
 
 // ------------------------------------------------------------------ E2M1
@@ -97,19 +98,40 @@ __device__ __forceinline__ uint32_t e2m1_pack4(float a, float b, float c, float 
   uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, 1.0f, 1);
 }
-__device__ __forceinline__ bool near_code_boundary(float y) {
-  return ((__float_as_uint(y) + 4u) & 0x1FFFFFu) <= 8u;
+// The low 21 bits of y + 4 moved to the top: y is near a code boundary when
+// this is at most kNearCode (the minimum over a block decides for the block).
+__device__ __forceinline__ uint32_t code_boundary_gap(float y) {
+  return (__float_as_uint(y) << 11) + (4u << 11);
 }
-__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g, uint32_t& lo,
-                                                  uint32_t& hi) {
+constexpr uint32_t kNearCode = 8u << 11;
+// The block scale byte from the block amax a:
+//   sf = E4M3_sat(fp32(fp32(a / 6) / g)).
+// c6g = recip6(g) = fp32(1 / fp32(6 g)), taken once per row or tensor. Then
+// z = fp32(a * c6g) is within 5 ulp of the two-division value, and the E4M3
+// rounding of a value only changes at points whose low 19 mantissa bits are
+// zero (the midpoints of the normal range, the half steps of the subnormal
+// grid), so unless z lies within 16 ulp of such a point (bit patterns
+// checked, zero, inf and NaN included) it encodes to the same byte; otherwise
+// the two divisions are taken. c6g = 0 (g outside [2^-100, 2^100], where
+// 6 g or its reciprocal could lose precision) always takes the divisions.
+__device__ __forceinline__ float recip6(float g) {
+  return (g >= 0x1p-100f && g <= 0x1p100f) ? 1.0f / (6.0f * g) : 0.0f;
+}
+__device__ __forceinline__ uint32_t block_scale_byte(float a, float g, float c6g) {
+  const float z = a * c6g;
+  if (((__float_as_uint(z) << 13) + (16u << 13)) <= (32u << 13)) return e4m3_encode_sat(a / 6.0f / g);
+  return e4m3_encode_sat(z);
+}
+
+__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g, float c6g,
+                                                  uint32_t& lo, uint32_t& hi) {
   float amax_b = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(x[i]));
   uint32_t sf = 0;
   float e = 0.0f;
   if (g > 0.0f) {
-    float t = amax_b / 6.0f;
-    sf = e4m3_encode_sat(t / g);
+    sf = block_scale_byte(amax_b, g, c6g);
     e = e4m3_decode(sf) * g;
   }
   lo = 0;
@@ -117,13 +139,13 @@ __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float g,
   if (e > 0.0f) {
     const float r = 1.0f / e;
     float y[16];
-    bool exact = !(r <= 3.4e38f);  // 1 / e overflowed
+    uint32_t gap = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       y[i] = x[i] * r;
-      exact |= near_code_boundary(y[i]);
+      gap = min(gap, code_boundary_gap(y[i]));
     }
-    if (exact) {
+    if (gap <= kNearCode || !(r <= 3.4e38f)) {  // or 1 / e overflowed
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = x[i] / e;
     }

@@ -84,6 +84,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, lo
     }
     g = wave_max(amax) * kRecipeConst;
   }
+  const float c6g = recip6(g);
   const int nblk_q = Lq / kBlock;
   uint2* qr = reinterpret_cast<uint2*>(q + row * (Lq / 2));
   uint8_t* sr = sf + row * nblk_q;
@@ -97,7 +98,7 @@ __device__ __forceinline__ void quantize_row_wave(const void* __restrict__ x, lo
       const int b = b0 + 64 * i;
       if (b < nblk) {
         uint32_t lo, hi;
-        const uint32_t s = quant_block16(v[i], g, lo, hi);
+        const uint32_t s = quant_block16(v[i], g, c6g, lo, hi);
         qr[b] = make_uint2(lo, hi);
         sr[b] = (uint8_t)s;
       }
@@ -153,6 +154,7 @@ __device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, l
     g = amax * kRecipeConst;
   }
   if (!active) return;
+  const float c6g = recip6(g);
   const int nblk_q = Lq / kBlock;
   uint2* qr = reinterpret_cast<uint2*>(q + row * (Lq / 2));
   uint8_t* sr = sf + row * nblk_q;
@@ -161,7 +163,7 @@ __device__ __forceinline__ void quantize_row_group(const void* __restrict__ x, l
     const int b = lt + 256 * i;
     if (b < nblk) {
       uint32_t lo, hi;
-      const uint32_t s = quant_block16(v[i], g, lo, hi);
+      const uint32_t s = quant_block16(v[i], g, c6g, lo, hi);
       qr[b] = make_uint2(lo, hi);
       sr[b] = (uint8_t)s;
     } else if (b < nblk_q) {  // padding block

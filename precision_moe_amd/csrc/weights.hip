@@ -1,13 +1,14 @@
 // Weight preparation: BF16 expert stacks -> NVFP4 in the prepared layout
 // [Megatron-LM #8262 . What is added, 'prepare_routed_nvfp4_weights'].
 //
-// Two kernels per FC matrix:
+// Three kernels per FC matrix:
 //   1. amax partials: each workgroup reduces max|w| over a 64K-element span of
 //      one expert (exact and order-free, so the result is deterministic);
-//   2. quantize: each workgroup owns one 32-row column block of one expert
-//      (column blocks past N, which pad the last 8-block column tile, are
-//      written as zeros),
-//      folds its expert's partials into amax, derives
+//   2. fold: one workgroup per expert folds its partials into amax and
+//      writes the expert's alpha;
+//   3. quantize: each workgroup owns eight 64-element chunks of one 32-row
+//      column block of one expert, read row by row in contiguous pieces (column blocks past N, which pad the last
+//      8-block column tile, are written as zeros), derives
 //        w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale)
 //      and quantizes every 16-block of its rows with g = alpha, writing codes
 //      and E4M3 scales straight into the prepared layout (see include/pmoe.h).
@@ -51,41 +52,62 @@ __global__ __launch_bounds__(256) void weight_amax_kernel(const uint16_t* __rest
         __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
-// grid (NBp, E) with NBp = NB rounded up to a multiple of 8. gated_I > 0
-// selects the gate/up interleave of a gated FC1. KC chunks of 64 cover Kd
-// (a multiple of 16) rounded up; blocks past Kd, rows past N (past I in each
-// half of a gated FC1) and whole padding column blocks are written as zeros.
-__global__ __launch_bounds__(256) void weight_quant_kernel(
-    const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int NBp, int KC,
-    const float* __restrict__ partials, int parts, const float* __restrict__ fold_a,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ alpha_out) {
-  const int p = blockIdx.x, e = blockIdx.y;
+// grid E: folds each expert's partial maxima into its amax, stored in place
+// of its first partial, and writes the expert's alpha.
+__global__ __launch_bounds__(256) void weight_amax_fold_kernel(float* __restrict__ partials, int parts,
+                                                               const float* __restrict__ fold_a,
+                                                               float* __restrict__ alpha_out) {
+  const int e = blockIdx.x;
   __shared__ float red[4];
   float m = 0.0f;
   for (int i = threadIdx.x; i < parts; i += 256) m = __builtin_fmaxf(m, partials[(long)e * parts + i]);
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) {
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    const float w_scale = 2688.0f / amax;  // +inf for an all-zero expert
+    partials[(long)e * parts] = amax;
+    alpha_out[e] = fold_a ? 1.0f / (w_scale * *fold_a) : 1.0f / w_scale;
+  }
+}
+
+// grid (NBp * KR, E): NBp = NB rounded up to a multiple of 8, KR = KC / 8
+// rounded up. Workgroup (p, kr) quantizes chunks 8*kr .. 8*kr + 7 of column
+// block p. gated_I > 0 selects the gate/up interleave of a gated FC1. KC
+// chunks of 64 cover Kd (a multiple of 16) rounded up; blocks past Kd, rows
+// past N (past I in each half of a gated FC1) and whole padding column
+// blocks are written as zeros.
+constexpr int kRoundChunks = 8;  // chunks of a column block per workgroup
+
+__global__ __launch_bounds__(256) void weight_quant_kernel(
+    const uint16_t* __restrict__ w, int N, int Kd, int gated_I, int NB, int NBp, int KC,
+    const float* __restrict__ amax_of, int parts, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int KR = (KC + kRoundChunks - 1) / kRoundChunks;
+  const int p = blockIdx.x / KR, c0 = (blockIdx.x - p * KR) * kRoundChunks, e = blockIdx.y;
+  const float amax = amax_of[(long)e * parts];
   const float w_scale = 2688.0f / amax;  // +inf for an all-zero expert
   const float alpha = 1.0f / w_scale;    // then 0
-  if (p == 0 && threadIdx.x == 0) alpha_out[e] = fold_a ? 1.0f / (w_scale * *fold_a) : alpha;
+  const float c6g = recip6(alpha);
 
   // Chunk c of column block p is one 1 KB code slab (+ 128 B of scales) at
-  // slab ((e*NT + p/8)*KC + c)*8 + p%8. Two chunks per round: thread t
-  // quantizes, of row t/8 of the column block, block (t%8)%4 of chunk
-  // c0 + (t%8)/4; the codes and scales go into LDS in slab order, then the
-  // two slabs are copied out with 16-byte stores (the prepared layout spreads
-  // a block's codes over lanes, so storing them directly would write each
-  // line several times over).
-  __shared__ uint32_t lcodes[2][256];
-  __shared__ uint32_t lscales[2][32];
+  // slab ((e*NT + p/8)*KC + c)*8 + p%8. The eight threads of row t/8 of the
+  // column block take its 32 16-element blocks in turn: thread t quantizes
+  // blocks t%8, t%8 + 8, t%8 + 16 and t%8 + 24 (block j = t%4 of chunks
+  // c0 + t%8/4, c0 + 2 + t%8/4, ...), so each pair of 16-byte loads of a
+  // wave covers eight rows x 256 contiguous bytes. The codes and scales go
+  // into LDS in slab order, then the eight slabs are copied out with 16-byte
+  // stores (the prepared layout spreads a block's codes over lanes, so
+  // storing them directly would write each line several times over).
+  __shared__ uint32_t lcodes[kRoundChunks][256];  // [chunk][lane * 4 + word]
+  __shared__ uint8_t lscales[kRoundChunks][128];  // [chunk][scale dword * 4 + byte]
   const long tile_base = ((long)e * (NBp / kColTileBlocks) + p / kColTileBlocks) * KC;
   const int pos = p % kColTileBlocks;
   const int tid = threadIdx.x;
   const int col = tid >> 3;  // row of the column block (0..31)
-  const int bl = tid & 7;    // block of the round: chunk bl/4, block bl%4 of that chunk
-  int n;                     // canonical row (only read when row_ok)
+  const int q = tid & 7;     // first block of this thread
+  int n;                     // canonical row
   bool row_ok;
   if (gated_I > 0) {
     const int r = kColBlock * (p >> 1) + col;  // row within the gate or the up half
@@ -95,47 +117,63 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
     n = kColBlock * p + col;
     row_ok = p < NB && n < N;
   }
-  const int cs = bl >> 2, j = bl & 3;
-  // block j of a chunk is half jj of k-step s; its row sits in 16-column
-  // block h of the position. Lane 32*jj + col%16 holds elements 0..7, lane
-  // + 16 elements 8..15, each as word 2h + s of its 16 bytes; the scale is
-  // byte 2h + s of dword col%16 + 16*jj.
-  const int s = j >> 1, jj = j & 1, h = col >> 4, n16 = col & 15;
-  const int lane_lo = 32 * jj + n16;
-  for (int c0 = 0; c0 < KC; c0 += 2) {
-    const int c = c0 + cs;
-    uint32_t lo = 0, hi = 0, sf = 0;
-    if (row_ok && c < KC && (4 * c + j) * kBlock < Kd) {
-      const uint4* src =
-          reinterpret_cast<const uint4*>(w + ((long)e * N + n) * Kd + (4 * c + j) * kBlock);
-      uint4 u0 = src[0], u1 = src[1];
-      uint32_t v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      float x[16];
+  // The expert's rows as one buffer: reads of blocks past Kd or of rows that
+  // do not exist get an offset past its end and return zeros, which quantize
+  // to zero codes and a zero scale.
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w + (long)e * N * Kd), (short)0, (int)((long)N * Kd * 2), 0x00020000);
+  const uint32_t row_off = row_ok ? (uint32_t)n * (uint32_t)Kd * 2u : 0x80000000u;
+  uint4 u[4][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
-        x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
-      }
-      sf = quant_block16(x, alpha, lo, hi);
+  for (int i = 0; i < 4; ++i) {
+    const int k = c0 * kChunk + kBlock * (8 * i + q);
+    const uint32_t off = k < Kd ? row_off + (uint32_t)k * 2u : 0x80000000u;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src, off + 16 * hf, 0, 0);
+      u[i][hf] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    lcodes[cs][lane_lo * 4 + 2 * h + s] = lo;
-    lcodes[cs][(lane_lo + 16) * 4 + 2 * h + s] = hi;
-    reinterpret_cast<uint8_t*>(lscales[cs])[(n16 + 16 * jj) * 4 + 2 * h + s] = (uint8_t)sf;
-    __syncthreads();
-    if (tid < 128) {  // codes: two slabs of 64 lanes x 16 bytes
-      const int k = tid >> 6, l = tid & 63;
-      if (c0 + k < KC) {
-        const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
-        reinterpret_cast<uint4*>(codes + slab * 1024)[l] = reinterpret_cast<const uint4*>(lcodes[k])[l];
-      }
-    } else if (tid < 144) {  // scales: two slabs of 8 x 16 bytes
-      const int k = (tid - 128) >> 3, q = (tid - 128) & 7;
-      if (c0 + k < KC) {
-        const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
-        reinterpret_cast<uint4*>(scales + slab * 128)[q] = reinterpret_cast<const uint4*>(lscales[k])[q];
-      }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all eight loads in flight before the first use
+  // Block j of a chunk is half jj = j%2 of k-step s = j/2; its row sits in
+  // 16-column block h of the position. Lane 32*jj + col%16 holds elements
+  // 0..7, lane + 16 elements 8..15, each as word 2h + s of its 16 bytes; the
+  // scale is byte 2h + s of dword col%16 + 16*jj.
+  const int h = col >> 4, n16 = col & 15, j = q & 3, jj = j & 1, s = j >> 1;
+  const int word = (32 * jj + n16) * 4 + 2 * h + s;
+  const int sbyte = (n16 + 16 * jj) * 4 + 2 * h + s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cl = 2 * i + (q >> 2);  // chunk of the workgroup
+    const uint32_t v[8] = {u[i][0].x, u[i][0].y, u[i][0].z, u[i][0].w,
+                           u[i][1].x, u[i][1].y, u[i][1].z, u[i][1].w};
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[2 * k] = bf16_to_f32(v[k] & 0xFFFFu);
+      x[2 * k + 1] = bf16_to_f32(v[k] >> 16);
     }
-    __syncthreads();
+    uint32_t lo, hi;
+    const uint32_t sf = quant_block16(x, alpha, c6g, lo, hi);
+    lcodes[cl][word] = lo;
+    lcodes[cl][word + 64] = hi;  // lane + 16
+    lscales[cl][sbyte] = (uint8_t)sf;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {  // codes: eight slabs of 64 lanes x 16 bytes
+    const int t = tid + 256 * r, k = t >> 6, l = t & 63;
+    if (c0 + k < KC) {
+      const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
+      reinterpret_cast<uint4*>(codes + slab * 1024)[l] = reinterpret_cast<const uint4*>(lcodes[k])[l];
+    }
+  }
+  if (tid < 64) {  // scales: eight slabs of 8 x 16 bytes
+    const int k = tid >> 3, t = tid & 7;
+    if (c0 + k < KC) {
+      const long slab = (tile_base + c0 + k) * kColTileBlocks + pos;
+      reinterpret_cast<uint4*>(scales + slab * 128)[t] = reinterpret_cast<const uint4*>(lscales[k])[t];
+    }
   }
 }
 
@@ -147,10 +185,13 @@ hipError_t launch_prepare_fc(const uint16_t* w, int E, int N, int Kd, int gated_
   weight_amax_kernel<<<dim3(parts, E), 256, 0, s>>>(w, per_expert, parts, partials);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  weight_amax_fold_kernel<<<E, 256, 0, s>>>(partials, parts, fold_a, alpha);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   const int NB = col_blocks(N, gated_I), KC = padded_k(Kd) / kChunk;
-  const int NBp = padded_col_blocks(NB);
-  weight_quant_kernel<<<dim3(NBp, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, NBp, KC, partials, parts,
-                                                   fold_a, codes, scales, alpha);
+  const int NBp = padded_col_blocks(NB), KR = (KC + kRoundChunks - 1) / kRoundChunks;
+  weight_quant_kernel<<<dim3(NBp * KR, E), 256, 0, s>>>(w, N, Kd, gated_I, NB, NBp, KC, partials, parts,
+                                                        codes, scales);
   return hipGetLastError();
 }
 
