@@ -511,6 +511,10 @@ def main():
                              "the steps",
                      "achieved": fc1_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": fc1_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "traffic_what": "HBM bytes of the step's launches of this kernel (both parts): "
+                                     "rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what it "
+                                     "reads for a plain device copy; null once the GEMM sources "
+                                     "differ from the ones measured",
                      "algorithmic_bytes": ab["fc1"], "span_us": fc1_span * 1e3,
                      "span_us_median": float(np.median(spans["fc1_span"])) * 1e3,
                      "launch_us": {"part1": float(np.mean(spans["fc1_part1"])) * 1e3,

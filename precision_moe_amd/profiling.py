@@ -7,9 +7,11 @@
         kernel name and n, also the average of that kernel's first n dispatches
     python -m precision_moe_amd.profiling traffic <fetch dir> <write dir> <copy fetch dir>
         <copy write dir> <copy bytes> <kernel substring> <workload> <out.txt> "<commands>"
+        [<launches per step>]
         HBM bytes per dispatch of one kernel from `--pmc FETCH_SIZE` and
         `--pmc WRITE_SIZE` runs, each scaled by what the same counter reads for
-        a plain device copy of known size
+        a plain device copy of known size, and per step (launches per step x
+        the mean per dispatch)
     python -m precision_moe_amd.profiling table <trace dir> <fetch dir> <write dir> <copy fetch dir>
         <copy write dir> <copy bytes> <mfma counter dir> <workload> <out.txt> "<commands>"
         every pmoe kernel: HBM bytes and GB/s, MFMA instructions and busy fraction
@@ -171,7 +173,12 @@ def write_spans(directory, workload, out, command, kernel, first, count):
         f.write("\n".join(lines) + "\n")
 
 
-def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, workload, out, command):
+def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, workload, out, command,
+                  launches=1):
+    """HBM bytes of `kernel` per dispatch from the FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the counter reads for a plain device copy of copy_bytes; with
+    launches > 1 (a kernel the step launches that many times, e.g. once per part of
+    the experts) also the bytes per step: launches x the mean per dispatch."""
     def one(d, counter):
         vals = {k: v for k, v in counter_means(d, counter).items() if kernel in k}
         if len(vals) != 1:
@@ -201,6 +208,8 @@ def write_traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, kernel, work
         f"fetch_factor={ff:.6f}",
         f"write_factor={wf:.6f}",
         f"hbm_bytes_per_dispatch={hbm:.0f}",
+        f"launches_per_step={launches}",
+        f"hbm_bytes_per_step={hbm * launches:.0f}",
     ]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -246,8 +255,9 @@ def write_table(kt_dir, fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, mfma_d
 
 
 def read_traffic(path, workload):
-    """HBM bytes per dispatch from a traffic summary, or None if absent, for another
-    workload, or measured with different GEMM sources."""
+    """HBM bytes per step (all of the kernel's launches in a step; per dispatch in
+    summaries that give no step figure) from a traffic summary, or None if absent,
+    for another workload, or measured with different GEMM sources."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -257,7 +267,7 @@ def read_traffic(path, workload):
             kv[k] = v
     if kv.get("workload") != workload or kv.get("source_sha256") != gemm_source_hash():
         return None
-    return float(kv["hbm_bytes_per_dispatch"])
+    return float(kv.get("hbm_bytes_per_step", kv["hbm_bytes_per_dispatch"]))
 
 
 if __name__ == "__main__":
@@ -267,7 +277,7 @@ if __name__ == "__main__":
         write_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], first)
     elif cmd == "traffic":
         write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7],
-                      sys.argv[8], sys.argv[9], sys.argv[10])
+                      sys.argv[8], sys.argv[9], sys.argv[10], int(sys.argv[11]) if len(sys.argv) > 11 else 1)
     elif cmd == "spans":
         write_spans(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], int(sys.argv[7]),
                     int(sys.argv[8]))
