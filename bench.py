@@ -410,12 +410,9 @@ def main():
     P_pt = pm.prepare_weights(w1, w2, input_scales=(a1, a2))
     del w1, w2
     torch.cuda.empty_cache()
-    xq_pt = torch.empty_like(xq)
-    xs_pt = torch.empty_like(xs)
 
-    def step_per_tensor():
-        pm.quantize_input_per_tensor(x, a1, out=(xq_pt, xs_pt))
-        pm.routed_moe_per_tensor(xq_pt, xs_pt, ids, wts, P_pt, a2, workspace=ws, out=out)
+    def step_per_tensor():  # the one-call forward, as the per-token step
+        pm.moe_forward(x, ids, wts, P_pt, recipe="per_tensor", a1=a1, a2=a2, workspace=ws, out=out)
 
     def step_w4a16():
         pm.routed_moe_w4a16(x, ids, wts, P, workspace=ws, out=out)

@@ -7,8 +7,9 @@
 //   2. fold: one workgroup per expert folds its partials into amax and
 //      writes the expert's alpha;
 //   3. quantize: each workgroup owns eight 64-element chunks of one 32-row
-//      column block of one expert, read row by row in contiguous pieces (column blocks past N, which pad the last
-//      8-block column tile, are written as zeros), derives
+//      column block of one expert, read row by row in contiguous pieces
+//      (column blocks past N, which pad the last 8-block column tile, are
+//      written as zeros); it derives
 //        w_scale = fp32(2688 / amax), alpha = fp32(1 / w_scale)
 //      and quantizes every 16-block of its rows with g = alpha, writing codes
 //      and E4M3 scales straight into the prepared layout (see include/pmoe.h).
