@@ -438,7 +438,10 @@ def main():
                      ("per_token_one_stream", step_one_stream),
                      ("per_token_fused_finalize", step_fused),
                      ("router_topk", step_router)):
-        for _ in range(max(args.warmup // 2, 2)):
+        # each recipe starts from a steady device: after idle or memory-bound
+        # work (the per-tensor weight preparation above) the first ~25-40 steps
+        # of any GPU work run slower
+        for _ in range(max(args.warmup, 30)):
             fn()
         torch.cuda.synchronize()
         ms = float(np.mean(timed_steps(torch, fn, args.steps)))
@@ -553,7 +556,8 @@ def main():
             OP = pm.prepare_weights(a.view(torch.bfloat16), b.view(torch.bfloat16))
             del a, b
             torch.cuda.empty_cache()
-        res, _ = run_workload(torch, pm, synth, ow, OP, dev, args.steps, max(args.warmup, 5))
+        # after this workload's weight preparation: warmed to a steady device first
+        res, _ = run_workload(torch, pm, synth, ow, OP, dev, args.steps, max(args.warmup, 30))
         others[name] = res
         log(f"[bench] {name}: median {res['step_us']['median']:.1f} us/step, "
             f"{res['tokens/s'] / 1e6:.3f} M tokens/s, FC1 span {res['fc1_in_step']['span_us']:.1f} us")
