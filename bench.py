@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cpu-experts", type=int, default=20,
                     help="the CPU oracle baseline runs all routes of this many experts")
-    ap.add_argument("--other-workloads", default="ep4_t512,large",
+    ap.add_argument("--other-workloads", default="ep4_t512,large,relu2,swiglu,tiny",
                     help="comma-separated further workloads timed in the same run ('' for none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
