@@ -387,8 +387,14 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
         a[rb][s2] = *reinterpret_cast<const AV*>(abuf + 16 * rb * kLdsRow + frag[half][s2]);
+    // Each position's fragments are decoded in one block of VALU work and then
+    // fed to its MFMAs in one block (scheduling barriers between them): the
+    // waves sharing a SIMD then alternate whole decode and MFMA phases, which
+    // co-execute better than the compiler's finer interleave (FC1 at the
+    // 4096-token shape 2 % faster, the 1024-token step unchanged).
     {
       const BFrag<AK> f(rq0[i], rs0[i]);  // column blocks 0, 1 of the wave
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -396,9 +402,11 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
           acc[rb][0] = mfma16(a[rb][s2], f.b[s2], acc[rb][0]);
           acc[rb][1] = mfma16(a[rb][s2], f.b[2 + s2], acc[rb][1]);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
     {
       const BFrag<AK> f(rq1[i], rs1[i]);  // column blocks 2, 3
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
