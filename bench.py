@@ -547,9 +547,9 @@ def main():
         ow = synth.WORKLOADS[name]
         same = (ow.index, ow.weight_epoch, ow.E, ow.N1, ow.H, ow.I) == (w.index, w.weight_epoch, w.E,
                                                                         w.N1, w.H, w.I)
-        if same:
+        if same and P is not None:
             OP = P
-        else:
+        else:  # other weights, or the main ones after an earlier workload freed them
             P = None
             torch.cuda.empty_cache()
             a, b = synth.all_weights(ow, device=dev)
