@@ -347,16 +347,21 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // B register ring: chunk c lives in slot c % kRing. Chunk c refills slot
-  // (c + kPrefetch) % kRing -- the slot chunk c - 1 has just finished
-  // decoding -- with chunk c + kPrefetch, so each slot keeps its registers
-  // around the loop and kPrefetch chunks stay in flight.
+  // B register ring: chunk c lives in slot c % kRing. Early refill: as soon
+  // as chunk c has decoded one position's codes and scales, it reloads that
+  // half of its slot with chunk c + kRing, so each load has almost kRing
+  // chunks of work to arrive in with no registers beyond the ring (a ring of
+  // 2 then hides about as much latency as a ring of 3 refilled per chunk:
+  // the NVFP4 half launches are 3 % faster). Otherwise (the atomic-finalize
+  // FC2, whose epilogue leaves no register for it) chunk c refills slot
+  // (c + kRing - 1) % kRing, which chunk c - 1 has finished, before it decodes.
   static_assert(kRing == 2 || kRing == 4, "the stage loop assumes a ring of 2 or 4 chunks");
-  constexpr int kPrefetch = kRing - 1;  // B chunks in flight ahead of the one in use
+  constexpr bool kEarly = MODE != kFc2Fused;
+  constexpr int kAhead = kEarly ? kRing : kRing - 1;  // chunks loaded before the loop
   uint4 rq0[kRing], rq1[kRing];
   uint32_t rs0[kRing], rs1[kRing];
 #pragma unroll
-  for (int i = 0; i < kPrefetch; ++i) {
+  for (int i = 0; i < kAhead; ++i) {
     const int ci = min(i, KC - 1);
     rq0[i] = load_q(bq_voff0, ci);
     rq1[i] = load_q(bq_voff1, ci);
@@ -371,15 +376,18 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
   lds_barrier();
 
   auto chunk = [&](const int c, const uint8_t* abuf, const int half, const int i) {
-    // Refill the slot freed by chunk c - 1 before decoding slot i; the
-    // scheduling barrier keeps these loads ahead of the decode.
-    const int r = (i + kPrefetch) % kRing;
-    const int cn = min(c + kPrefetch, KC - 1);
-    rq0[r] = load_q(bq_voff0, cn);
-    rq1[r] = load_q(bq_voff1, cn);
-    rs0[r] = load_s(bs_voff0, cn);
-    rs1[r] = load_s(bs_voff1, cn);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!kEarly) {
+      // Refill the slot freed by chunk c - 1 before decoding slot i; the
+      // scheduling barrier keeps these loads ahead of the decode.
+      const int r = (i + kRing - 1) % kRing;
+      const int cn = min(c + kRing - 1, KC - 1);
+      rq0[r] = load_q(bq_voff0, cn);
+      rq1[r] = load_q(bq_voff1, cn);
+      rs0[r] = load_s(bs_voff0, cn);
+      rs1[r] = load_s(bs_voff1, cn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int cn = min(c + kRing, KC - 1);  // early refill: the chunk slot i holds next
     using AV = typename BFrag<AK>::V;
     AV a[NRB][2];
 #pragma unroll
@@ -395,6 +403,11 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     {
       const BFrag<AK> f(rq0[i], rs0[i]);  // column blocks 0, 1 of the wave
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kEarly) {
+        rq0[i] = load_q(bq_voff0, cn);
+        rs0[i] = load_s(bs_voff0, cn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -407,6 +420,11 @@ __device__ __forceinline__ void fc_tile(const FcParams& P, uint8_t (*a_lds)[kLds
     {
       const BFrag<AK> f(rq1[i], rs1[i]);  // column blocks 2, 3
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kEarly) {
+        rq1[i] = load_q(bq_voff1, cn);
+        rs1[i] = load_s(bs_voff1, cn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
