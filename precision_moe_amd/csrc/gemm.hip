@@ -22,7 +22,8 @@
 //     9 KB slab, so a workgroup streams a single sequential region; per chunk
 //     and position each lane loads one 16-byte span (1 KB per wave-load) and
 //     one dword of four E4M3 scales, by buffer loads with scalar chunk
-//     offsets. Loads run 3 (or 1) chunks ahead in a register ring; decoding
+//     offsets, through a register ring of 4 (or 2) chunks that is refilled as
+//     soon as a position has been decoded; decoding
 //     happens in registers straight into MFMA operand order (each block scale
 //     multiplied into its 16 decoded values, exact in FP16), and every decoded
 //     B fragment feeds all row blocks.
@@ -64,11 +65,11 @@ constexpr int kBufFlags = 0x00020000;              // raw buffer, 32-bit data fo
 constexpr int kCpolNT = 2;                         // cache-policy operand: non-temporal
 constexpr int kGroup = 2;                          // stages per loop iteration
 constexpr int kStages = 2;                         // LDS A stage buffers (double buffer)
-// B register ring (chunks per wave, RING - 1 of them in flight) and resident
-// workgroups per CU. A whole-expert-set launch keeps 4 chunks in flight at 2
-// workgroups per CU (180 VGPRs). The half launches of the NVFP4 recipes run
-// two at a time on two streams; there a ring of 2 (168 VGPRs) lets 3
-// workgroups share a CU, which fills the CUs better than a deeper ring.
+// B register ring (chunks per wave) and resident workgroups per CU. A
+// whole-expert-set launch uses a ring of 4 at 2 workgroups per CU (186-192
+// VGPRs). The half launches of the NVFP4 recipes run two at a time on two
+// streams; there a ring of 2 (166-168 VGPRs) lets 3 workgroups share a CU,
+// which fills the CUs better than a deeper ring.
 template <int AK, bool HALF>
 struct FcConfig {
   static constexpr int kRing = (HALF && AK == 0) ? 2 : 4;
