@@ -113,32 +113,37 @@ def test_expert_count_edges(pm, case):
 
 @pytest.mark.parametrize("H,I", [(16, 16), (64, 48), (128, 96), (192, 64)])
 @pytest.mark.parametrize("act", ["relu2", "swiglu"])
-@pytest.mark.parametrize("recipe", ["per_token", "w4a16"])
+@pytest.mark.parametrize("recipe", ["per_token", "w4a16", "per_token_fused"])
 def test_short_reductions(pm, H, I, act, recipe):
     """Reductions of one, two and three 64-element chunks (fewer chunks than
     the weight register ring holds, so every prefetch past the end is clamped
     to the last chunk): 2048 routes, run on one stream (whole launches) and
-    split over two (half launches), NVFP4 and W4A16; bit-equal, and equal to
-    the oracle to the per-token tolerance for every token."""
+    split over two (half launches), NVFP4 and W4A16, and the order-free
+    finalize (whose FC2 refills its ring the other way); bit-equal across the
+    two (ordered finalize), and equal to the oracle to the per-token tolerance
+    for every token."""
     import torch
     rng = np.random.default_rng(H * 1000 + I + (act == "swiglu"))
     T, K, E = 1024, 2, 8
     ids = np.argsort(rng.standard_normal((T, E)), axis=1)[:, :K].astype(np.int32)
     w1, w2, x, wts, P = _moe_case(pm, rng, T, K, E, H, I, act, ids)
-    outs = [pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P, recipe=recipe, streams=s)
-            for s in (1, 2)]
+    fused = recipe == "per_token_fused"
+    kw = dict(recipe="per_token", finalize="fused") if fused else dict(recipe=recipe)
+    outs = [pm.moe_forward(dev_bf16(x), dev(ids), dev(wts), P, streams=s, **kw) for s in (1, 2)]
     _sync()
-    assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16))
+    if not fused:  # the atomic adds of the fused finalize land in any order
+        assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16))
     W = om.prepare_weights(w1, w2)
-    if recipe == "per_token":
+    if recipe == "w4a16":
+        res = orc.routed_moe_recipe("weight_only", x, ids, wts, W, act)
+    else:
         xq, xs, xg = oq.quantize_input_per_token(x)
         res = om.routed_moe(xq, xs, xg, ids, wts, W, act)
-    else:
-        res = orc.routed_moe_recipe("weight_only", x, ids, wts, W, act)
-    got = bf16_to_f32(bf16_bits(outs[0])).astype(np.float64)
     want = bf16_to_f32(res.out).astype(np.float64)
-    err = np.abs(got - want).max(axis=1)
-    assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
+    for o in outs:
+        got = bf16_to_f32(bf16_bits(o)).astype(np.float64)
+        err = np.abs(got - want).max(axis=1)
+        assert np.all(err <= 1e-2 * np.abs(want).max(axis=1)), err / np.abs(want).max(axis=1)
 
 
 @pytest.mark.parametrize("T", [2048, 2049])
