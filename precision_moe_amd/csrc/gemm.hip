@@ -22,7 +22,7 @@
 //     9 KB slab, so a workgroup streams a single sequential region; per chunk
 //     and position each lane loads one 16-byte span (1 KB per wave-load) and
 //     one dword of four E4M3 scales, by buffer loads with scalar chunk
-//     offsets, through a register ring of 4 (or 2) chunks that is refilled as
+//     offsets, through a register ring of 2 (W4A16: 4) chunks that is refilled as
 //     soon as a position has been decoded; decoding
 //     happens in registers straight into MFMA operand order (each block scale
 //     multiplied into its 16 decoded values, exact in FP16), and every decoded
@@ -65,15 +65,17 @@ constexpr int kBufFlags = 0x00020000;              // raw buffer, 32-bit data fo
 constexpr int kCpolNT = 2;                         // cache-policy operand: non-temporal
 constexpr int kGroup = 2;                          // stages per loop iteration
 constexpr int kStages = 2;                         // LDS A stage buffers (double buffer)
-// B register ring (chunks per wave) and resident workgroups per CU. A
-// whole-expert-set launch uses a ring of 4 at 2 workgroups per CU (186-192
-// VGPRs). The half launches of the NVFP4 recipes run two at a time on two
-// streams; there a ring of 2 (166-168 VGPRs) lets 3 workgroups share a CU,
-// which fills the CUs better than a deeper ring.
-template <int AK, bool HALF>
+// B register ring (chunks per wave) and resident workgroups per CU. The NVFP4
+// recipes use a ring of 2 (166-168 VGPRs), which lets 3 workgroups share a CU:
+// with the early refill (each load has almost two chunks of work to arrive
+// in) that beats a ring of 4 at 2 workgroups per CU, by 6 % for FC1 as one
+// launch at the 1024-token EP4 shape. W4A16 (AK = 1: BF16 activations, more
+// registers for its decode) keeps a ring of 4 at 2 workgroups per CU
+// (200-204 VGPRs).
+template <int AK>
 struct FcConfig {
-  static constexpr int kRing = (HALF && AK == 0) ? 2 : 4;
-  static constexpr int kWgPerCu = (HALF && AK == 0) ? 3 : 2;
+  static constexpr int kRing = AK == 0 ? 2 : 4;
+  static constexpr int kWgPerCu = AK == 0 ? 3 : 2;
 };
 
 __host__ __device__ int fc_col_tiles(int NB) { return padded_col_blocks(NB) / kColTileBlocks; }
@@ -551,21 +553,21 @@ __device__ __forceinline__ void fc_block(const FcParams& P, uint8_t (*a_lds)[kLd
 
 // One launch over the tiles of every local expert.
 template <int MODE, int AK>
-__global__ __launch_bounds__(kThreads, (FcConfig<AK, false>::kWgPerCu)) void fc_kernel(FcParams P) {
+__global__ __launch_bounds__(kThreads, (FcConfig<AK>::kWgPerCu)) void fc_kernel(FcParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
   __shared__ float s_row[kTileM];
-  fc_block<MODE, AK, FcConfig<AK, false>::kRing>(P, a_lds, a_row, s_row);
+  fc_block<MODE, AK, FcConfig<AK>::kRing>(P, a_lds, a_row, s_row);
 }
 
 // The same code over one half of the experts (P.part = 1 or 2); a kernel of
 // its own name so that a trace tells the half launches from the whole ones.
 template <int MODE, int AK>
-__global__ __launch_bounds__(kThreads, (FcConfig<AK, true>::kWgPerCu)) void fc_half_kernel(FcParams P) {
+__global__ __launch_bounds__(kThreads, (FcConfig<AK>::kWgPerCu)) void fc_half_kernel(FcParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kStages][kLdsStage];
   __shared__ int a_row[kTileM];
   __shared__ float s_row[kTileM];
-  fc_block<MODE, AK, FcConfig<AK, true>::kRing>(P, a_lds, a_row, s_row);
+  fc_block<MODE, AK, FcConfig<AK>::kRing>(P, a_lds, a_row, s_row);
 }
 
 template <int MODE, int AK>
