@@ -126,6 +126,25 @@ def test_weight_scale_and_invariants():
     assert az == 0 and not qz.any() and not sfz.any()
 
 
+def test_weight_scale_exact_at_powers_of_two():
+    """Where amax / 2688 is a power of two, w_scale = 2688 / amax and its
+    reciprocal are exact under any rounding, so alpha must equal amax / 2688
+    bit for bit: pins the recipe constant 2688 = 448 * 6 and the reciprocal
+    structure of the per-expert scale (not only to within 2 ulp)."""
+    for k in range(-40, 41, 5):
+        amax = np.float32(2688.0 * 2.0 ** k)
+        w = np.zeros((2, 32), F32)
+        w[1, 17] = amax
+        w[0, 3] = -amax * np.float32(0.25)
+        a, s = weight_global_scale(w)
+        assert np.float32(a) == np.float32(2.0 ** k), (k, a)
+        assert np.float32(s) == np.float32(2.0 ** -k), (k, s)
+        # the element at amax encodes as code 6 (0x7) under the top block scale 448
+        q, sf, alpha = quantize_weight_matrix(_bf16(w))
+        assert np.float32(alpha) == np.float32(2.0 ** k)
+        assert sf[1, 1] == 0x7E and unpack_nibbles(q)[1, 17] == 0x7
+
+
 def test_weight_dequant_error_small():
     rng = np.random.default_rng(16)
     w = (rng.standard_normal((128, 512)) * 0.02).astype(F32)
