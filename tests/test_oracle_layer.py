@@ -144,6 +144,30 @@ def test_fused_finalize_equals_exact_sum_of_fp32_terms():
         assert np.array_equal(got[t], want)
 
 
+def test_fused_finalize_closed_form_on_exact_terms():
+    """Integer z values and weights 1 or 2: every product and every partial
+    sum is an integer of magnitude at most 64, exact in FP32 and in BF16, so
+    the order-free finalize must return the integer sums themselves (computed
+    here with Python integers), skip invalid routes, and give +0 for a token
+    with none."""
+    rng = np.random.default_rng(47)
+    T, K, H, R = 6, 4, 16, 12
+    zi = rng.integers(-8, 9, (R, H))
+    wi = rng.integers(1, 3, (T, K))
+    rr = rng.integers(0, R, T * K).astype(np.int32)
+    rr[[1, 6, 7]] = -1
+    rr[4 * K:5 * K] = -1                                 # token 4: no valid route
+    got = bf16_to_f32(finalize_fused(zi.astype(np.float32), rr, wi.astype(np.float32), T, K))
+    for t in range(T):
+        want = [0] * H
+        for j in range(K):
+            r = int(rr[t * K + j])
+            if r >= 0:
+                want = [want[n] + int(wi[t, j]) * int(zi[r, n]) for n in range(H)]
+        assert got[t].tolist() == [float(v) for v in want], t
+    assert not np.signbit(got[4]).any() and not got[4].any()
+
+
 def test_fused_pipeline_close_to_ordered_and_brute_force():
     x, w1, w2, ids, wts = _case(46, T=16, act="relu2")
     q = quantize_input_per_token(x)
